@@ -1,0 +1,321 @@
+// C-ABI entry points of libkvsel: argument checks, workspace carving and the
+// launch sequence of one chunk.  Every check runs on the host before anything
+// is enqueued; no C++ exception leaves this file.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/kvsel.h"
+#include "launch.h"
+
+using namespace kvsel;
+
+namespace {
+
+thread_local std::string g_err;
+
+kvsel_status fail(kvsel_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+kvsel_status hip_check(hipError_t e, const char* what) {
+    if (e == hipSuccess) return KVSEL_OK;
+    return fail(KVSEL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define KVSEL_TRY(expr, what)                          \
+    do {                                               \
+        kvsel_status _s = hip_check((expr), (what));   \
+        if (_s != KVSEL_OK) return _s;                 \
+    } while (0)
+
+constexpr int64_t kMaxLen = int64_t(1) << 30;   // positions fit int32 kernel arithmetic
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// ----------------------------------------------------------------------------- checks
+
+kvsel_status check_heads(const kvsel_heads* h) {
+    if (!h) return fail(KVSEL_ERR_INVALID_ARG, "heads is NULL");
+    if (h->h_q < 1 || h->h_kv < 1) return fail(KVSEL_ERR_INVALID_ARG, "h_q=%d h_kv=%d must be >= 1", h->h_q, h->h_kv);
+    if (h->h_q % h->h_kv) return fail(KVSEL_ERR_INVALID_ARG, "h_q=%d is not a multiple of h_kv=%d", h->h_q, h->h_kv);
+    if (h->dtype != KVSEL_F32 && h->dtype != KVSEL_BF16) return fail(KVSEL_ERR_INVALID_ARG, "dtype=%d unknown", h->dtype);
+    if (h->d != 64 && h->d != 128) return fail(KVSEL_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", h->d);
+    if (!std::isfinite(h->scale) || h->scale < 0.0f) return fail(KVSEL_ERR_INVALID_ARG, "scale must be finite and >= 0");
+    return KVSEL_OK;
+}
+
+kvsel_status check_batch(const kvsel_batch* b, bool need_lens, int64_t* t_max) {
+    if (!b) return fail(KVSEL_ERR_INVALID_ARG, "batch is NULL");
+    if (b->batch < 1) return fail(KVSEL_ERR_INVALID_ARG, "batch=%d must be >= 1", b->batch);
+    if (b->chunk_len < 1 || b->chunk_len > kMaxLen) return fail(KVSEL_ERR_INVALID_ARG, "chunk_len=%d out of range", b->chunk_len);
+    *t_max = 0;
+    if (!need_lens) return KVSEL_OK;
+    if (!b->prior_len_host || !b->prior_len_dev) return fail(KVSEL_ERR_INVALID_ARG, "prior_len_host/prior_len_dev is NULL");
+    for (int i = 0; i < b->batch; ++i) {
+        const int64_t T = b->prior_len_host[i];
+        if (T < 0 || T + b->chunk_len > kMaxLen) return fail(KVSEL_ERR_INVALID_ARG, "prior_len[%d]=%lld out of range", i, (long long)T);
+        if (T > *t_max) *t_max = T;
+    }
+    return KVSEL_OK;
+}
+
+kvsel_status check_params(const kvsel_params* p) {
+    if (!p) return fail(KVSEL_ERR_INVALID_ARG, "params is NULL");
+    if (p->n_q < 1) return fail(KVSEL_ERR_INVALID_ARG, "n_q=%d must be >= 1", p->n_q);
+    if (p->budget < 1) return fail(KVSEL_ERR_INVALID_ARG, "budget=%d must be >= 1", p->budget);
+    return KVSEL_OK;
+}
+
+// extra = rows past T_b that the call writes (chunk_len for prefill, 0 for select)
+kvsel_status check_cache(const kvsel_cache* c, const kvsel_batch* b, int extra) {
+    if (!c) return fail(KVSEL_ERR_INVALID_ARG, "cache is NULL");
+    if (!c->k || !c->v) return fail(KVSEL_ERR_INVALID_ARG, "cache k/v is NULL");
+    if (!aligned16(c->k) || !aligned16(c->v)) return fail(KVSEL_ERR_INVALID_ARG, "cache k/v must be 16-byte aligned");
+    if (c->block_size < 0) return fail(KVSEL_ERR_INVALID_ARG, "block_size=%d < 0", c->block_size);
+    if (c->capacity < 1) return fail(KVSEL_ERR_INVALID_ARG, "cache capacity=%lld < 1", (long long)c->capacity);
+    for (int i = 0; i < b->batch; ++i) {
+        const int64_t need = b->prior_len_host[i] + extra;
+        if (c->block_size == 0) {
+            if (need > c->capacity)
+                return fail(KVSEL_ERR_INVALID_ARG, "sequence %d needs %lld cache rows, capacity is %lld", i, (long long)need, (long long)c->capacity);
+        } else {
+            if (!c->block_table) return fail(KVSEL_ERR_INVALID_ARG, "paged cache without block_table");
+            const int64_t blocks = (need + c->block_size - 1) / c->block_size;
+            if (blocks > c->max_blocks_per_seq)
+                return fail(KVSEL_ERR_INVALID_ARG, "sequence %d needs %lld blocks, block table holds %d", i, (long long)blocks, c->max_blocks_per_seq);
+        }
+    }
+    return KVSEL_OK;
+}
+
+CacheView make_view(const kvsel_cache* c, const kvsel_heads* h) {
+    CacheView v;
+    v.k = static_cast<char*>(c->k);
+    v.v = static_cast<char*>(c->v);
+    v.capacity = c->capacity;
+    v.block_size = c->block_size;
+    v.max_blocks = c->max_blocks_per_seq;
+    v.block_table = c->block_table;
+    v.h_kv = h->h_kv;
+    v.row_bytes = h->d * (h->dtype == KVSEL_BF16 ? 2 : 4);
+    return v;
+}
+
+SelShape make_shape(const kvsel_heads* h, const kvsel_batch* b, const kvsel_params* p, int64_t t_max) {
+    SelShape s;
+    s.batch = b->batch;
+    s.h_q = h->h_q;
+    s.h_kv = h->h_kv;
+    s.G = h->h_q / h->h_kv;
+    s.d = h->d;
+    s.C = b->chunk_len;
+    s.esz = h->dtype == KVSEL_BF16 ? 2 : 4;
+    s.nqp = p ? (p->n_q < b->chunk_len ? p->n_q : b->chunk_len) : 0;
+    if (s.esz == 4) s.nq_pad = s.nqp;                                     // VALU scan: exact rows
+    else if (s.nqp == 1 && s.G <= 16) s.nq_pad = 1;                       // one query row per head
+    else s.nq_pad = static_cast<int>(round_up(s.nqp, 32));                // MFMA scan: 32-row blocks
+    s.budget = p ? p->budget : 0;
+    s.t_max = t_max;
+    return s;
+}
+
+// ----------------------------------------------------------------------------- workspace layout
+
+struct Layout {
+    size_t qcos, qrn, keep, qsel, rq, scores, idx, nsel, kall, vall, total;
+    int nk_pad;
+};
+
+Layout layout(const SelShape& s, bool with_attn) {
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    const size_t bh = size_t(s.batch) * s.h_q, bg = size_t(s.batch) * s.h_kv;
+    L.qcos = take(bh * s.C * 4);
+    L.qrn = take(bh * s.C * 4);
+    L.keep = take(bh * s.nqp * 4);
+    L.qsel = take(bg * s.G * s.nq_pad * s.d * s.esz);
+    L.rq = take(bg * s.G * s.nq_pad * 4);
+    L.scores = take(bg * (s.t_max > 0 ? s.t_max : 1) * 4);
+    L.idx = take(bg * s.budget * 4);
+    L.nsel = take(size_t(s.batch) * 4);
+    const int64_t nsel_max = s.budget < s.t_max ? s.budget : s.t_max;
+    L.nk_pad = static_cast<int>(round_up(nsel_max + s.C, 64));
+    if (with_attn) {
+        L.kall = take(bg * L.nk_pad * s.d * s.esz);
+        L.vall = take(bg * L.nk_pad * s.d * s.esz);
+    }
+    L.total = off;
+    return L;
+}
+
+template <typename P> P* at(void* ws, size_t off) { return reinterpret_cast<P*>(static_cast<char*>(ws) + off); }
+
+kvsel_status check_ws(void* ws, size_t have, size_t need) {
+    if (need > have) return fail(KVSEL_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+    if (!ws) return fail(KVSEL_ERR_WORKSPACE, "workspace is NULL");
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(KVSEL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    return KVSEL_OK;
+}
+
+// Steps 1-3 into idx (shared by select and prefill_chunk).
+kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, const CacheView& cv, void* ws,
+                        const Layout& L, int32_t* idx, int32_t* q_keep, float* scores, hipStream_t st) {
+    bool any = false;
+    for (int i = 0; i < b->batch; ++i) any |= b->prior_len_host[i] > s.budget;
+    const int64_t* T = b->prior_len_dev;
+    float* S = scores ? scores : at<float>(ws, L.scores);
+    if (any) {
+        int32_t* keep = q_keep ? q_keep : at<int32_t>(ws, L.keep);
+        KVSEL_TRY(launch_qstats(s, q, T, at<float>(ws, L.qcos), at<float>(ws, L.qrn), st), "query statistics");
+        KVSEL_TRY(launch_topk(s.batch * s.h_q, s.h_q, at<float>(ws, L.qcos), s.C, T, s.C, s.budget, s.nqp, keep, s.nqp,
+                              1, st), "query top-k");
+        KVSEL_TRY(launch_pack_qsel(s, q, keep, s.nqp, at<float>(ws, L.qrn), T, at<void>(ws, L.qsel), at<float>(ws, L.rq), st),
+                  "query packing");
+        KVSEL_TRY(launch_scan(s, at<void>(ws, L.qsel), at<float>(ws, L.rq), cv, T, S, s.t_max, st), "key scan");
+    }
+    KVSEL_TRY(launch_topk(s.batch * s.h_kv, s.h_kv, S, s.t_max, T, 0, s.budget, static_cast<int>(s.budget), idx,
+                          s.budget, 0, st), "key top-B");
+    return KVSEL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvsel_last_error(void) { return g_err.c_str(); }
+
+int32_t kvsel_version(void) { return 100; }
+
+kvsel_status kvsel_workspace_size(const kvsel_heads* heads, const kvsel_batch* batch, const kvsel_params* params,
+                                  size_t* bytes) {
+    g_err.clear();
+    kvsel_status st;
+    int64_t t_max;
+    if ((st = check_heads(heads)) || (st = check_batch(batch, true, &t_max)) || (st = check_params(params))) return st;
+    if (!bytes) return fail(KVSEL_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = layout(make_shape(heads, batch, params, t_max), true).total;
+    return KVSEL_OK;
+}
+
+kvsel_status kvsel_sparse_attn_workspace_size(const kvsel_heads* heads, const kvsel_batch* batch, int32_t n_sel_max,
+                                              size_t* bytes) {
+    g_err.clear();
+    kvsel_status st;
+    int64_t t_max;
+    if ((st = check_heads(heads)) || (st = check_batch(batch, false, &t_max))) return st;
+    if (n_sel_max < 0 || n_sel_max > kMaxLen) return fail(KVSEL_ERR_INVALID_ARG, "n_sel_max=%d out of range", n_sel_max);
+    if (!bytes) return fail(KVSEL_ERR_INVALID_ARG, "bytes is NULL");
+    SelShape s = make_shape(heads, batch, nullptr, 0);
+    const int nk_pad = static_cast<int>(round_up(int64_t(n_sel_max) + s.C, 64));
+    const size_t kv = size_t(s.batch) * s.h_kv * nk_pad * s.d * s.esz;
+    *bytes = align256(size_t(s.batch) * 4) + 2 * align256(kv);
+    return KVSEL_OK;
+}
+
+kvsel_status kvsel_select(const kvsel_heads* heads, const kvsel_batch* batch, const kvsel_params* params, const void* q,
+                          const kvsel_cache* cache, int32_t* idx, void* k_sel, void* v_sel, int32_t* q_keep,
+                          float* scores, void* workspace, size_t workspace_bytes, void* stream) {
+    g_err.clear();
+    kvsel_status st;
+    int64_t t_max;
+    if ((st = check_heads(heads)) || (st = check_batch(batch, true, &t_max)) || (st = check_params(params)) ||
+        (st = check_cache(cache, batch, 0)))
+        return st;
+    if (!q || !aligned16(q)) return fail(KVSEL_ERR_INVALID_ARG, "q is NULL or not 16-byte aligned");
+    if (!idx) return fail(KVSEL_ERR_INVALID_ARG, "idx is NULL");
+    if ((k_sel == nullptr) != (v_sel == nullptr)) return fail(KVSEL_ERR_INVALID_ARG, "give both k_sel and v_sel, or neither");
+    if (k_sel && (!aligned16(k_sel) || !aligned16(v_sel))) return fail(KVSEL_ERR_INVALID_ARG, "k_sel/v_sel must be 16-byte aligned");
+    const SelShape s = make_shape(heads, batch, params, t_max);
+    const Layout L = layout(s, false);
+    if ((st = check_ws(workspace, workspace_bytes, L.total))) return st;
+    const CacheView cv = make_view(cache, heads);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if ((st = run_select(s, batch, q, cv, workspace, L, idx, q_keep, scores, hs))) return st;
+    if (k_sel) KVSEL_TRY(launch_gather(s, cv, batch->prior_len_dev, idx, s.budget, k_sel, v_sel, hs), "gather");
+    return KVSEL_OK;
+}
+
+kvsel_status kvsel_sparse_attn(const kvsel_heads* heads, const kvsel_batch* batch, const void* q, const void* k_sel,
+                               const void* v_sel, const int32_t* n_sel, int32_t n_sel_max, const void* k_chunk,
+                               const void* v_chunk, void* out, int32_t out_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    g_err.clear();
+    kvsel_status st;
+    int64_t t_max;
+    if ((st = check_heads(heads)) || (st = check_batch(batch, false, &t_max))) return st;
+    if (n_sel_max < 0 || n_sel_max > kMaxLen) return fail(KVSEL_ERR_INVALID_ARG, "n_sel_max=%d out of range", n_sel_max);
+    if (!q || !k_chunk || !v_chunk || !out || !n_sel) return fail(KVSEL_ERR_INVALID_ARG, "q/k_chunk/v_chunk/out/n_sel is NULL");
+    if (n_sel_max > 0 && (!k_sel || !v_sel)) return fail(KVSEL_ERR_INVALID_ARG, "k_sel/v_sel is NULL");
+    if (!aligned16(q) || !aligned16(k_chunk) || !aligned16(v_chunk) || !aligned16(out) || !aligned16(k_sel) || !aligned16(v_sel))
+        return fail(KVSEL_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    if (out_dtype != KVSEL_F32 && out_dtype != KVSEL_BF16) return fail(KVSEL_ERR_INVALID_ARG, "out_dtype=%d unknown", out_dtype);
+    size_t need;
+    if ((st = kvsel_sparse_attn_workspace_size(heads, batch, n_sel_max, &need))) return st;
+    if ((st = check_ws(workspace, workspace_bytes, need))) return st;
+    const SelShape s = make_shape(heads, batch, nullptr, 0);
+    const int nk_pad = static_cast<int>(round_up(int64_t(n_sel_max) + s.C, 64));
+    const size_t kv = size_t(s.batch) * s.h_kv * nk_pad * s.d * s.esz;
+    int32_t* nsel_ws = at<int32_t>(workspace, 0);
+    void* kall = at<void>(workspace, align256(size_t(s.batch) * 4));
+    void* vall = at<void>(workspace, align256(size_t(s.batch) * 4) + align256(kv));
+    PackSrc src{};
+    src.k_compact = k_sel;
+    src.v_compact = v_sel;
+    src.n_sel = n_sel;
+    src.n_sel_max = n_sel_max;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const float scale = heads->scale > 0.0f ? heads->scale : 1.0f / std::sqrt(static_cast<float>(heads->d));
+    KVSEL_TRY(launch_pack(s, src, k_chunk, v_chunk, nk_pad, kall, vall, nsel_ws, hs), "pack");
+    KVSEL_TRY(launch_attn(s, q, kall, vall, nsel_ws, nk_pad, scale, out, out_dtype == KVSEL_F32, hs), "attention");
+    return KVSEL_OK;
+}
+
+kvsel_status kvsel_prefill_chunk(const kvsel_heads* heads, const kvsel_batch* batch, const kvsel_params* params,
+                                 const void* q, const void* k_chunk, const void* v_chunk, const kvsel_cache* cache,
+                                 void* out, int32_t out_dtype, int32_t* idx, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    g_err.clear();
+    kvsel_status st;
+    int64_t t_max;
+    if ((st = check_heads(heads)) || (st = check_batch(batch, true, &t_max)) || (st = check_params(params)) ||
+        (st = check_cache(cache, batch, batch->chunk_len)))
+        return st;
+    if (!q || !k_chunk || !v_chunk || !out) return fail(KVSEL_ERR_INVALID_ARG, "q/k_chunk/v_chunk/out is NULL");
+    if (!aligned16(q) || !aligned16(k_chunk) || !aligned16(v_chunk) || !aligned16(out))
+        return fail(KVSEL_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    if (out_dtype != KVSEL_F32 && out_dtype != KVSEL_BF16) return fail(KVSEL_ERR_INVALID_ARG, "out_dtype=%d unknown", out_dtype);
+    const SelShape s = make_shape(heads, batch, params, t_max);
+    const Layout L = layout(s, true);
+    if ((st = check_ws(workspace, workspace_bytes, L.total))) return st;
+    const CacheView cv = make_view(cache, heads);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int32_t* idx_buf = idx ? idx : at<int32_t>(workspace, L.idx);
+    if ((st = run_select(s, batch, q, cv, workspace, L, idx_buf, nullptr, nullptr, hs))) return st;
+    PackSrc src{};
+    src.cache = &cv;
+    src.prior_len = batch->prior_len_dev;
+    src.budget = s.budget;
+    src.idx = idx_buf;
+    src.idx_stride = s.budget;
+    int32_t* nsel = at<int32_t>(workspace, L.nsel);
+    const float scale = heads->scale > 0.0f ? heads->scale : 1.0f / std::sqrt(static_cast<float>(heads->d));
+    KVSEL_TRY(launch_pack(s, src, k_chunk, v_chunk, L.nk_pad, at<void>(workspace, L.kall), at<void>(workspace, L.vall),
+                          nsel, hs), "pack");
+    KVSEL_TRY(launch_attn(s, q, at<void>(workspace, L.kall), at<void>(workspace, L.vall), nsel, L.nk_pad, scale, out,
+                          out_dtype == KVSEL_F32, hs), "attention");
+    KVSEL_TRY(launch_append(s, cv, batch->prior_len_dev, k_chunk, v_chunk, hs), "append");
+    return KVSEL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,323 @@
+// Attention of every chunk query over its KV head's compacted prior keys (all
+// visible) plus the chunk's own keys (causal), online softmax in fp32.
+//
+// QuoKA article ("Qualcomm QuoKA", itsolotime.com), Fig. 1(a): the compacted
+// cache feeds a dense attention kernel.  QUILT page (chiosa.app, "In parole
+// semplici"): queries that selected the same KV entries are grouped so those
+// entries are loaded once and reused.  Here every query of a chunk that maps
+// to one KV head shares the same compacted set, so a workgroup packs
+// (token, head-in-group) rows of all G heads of a KV head and stages each key
+// tile in LDS once for all of them.  Multi-query attention page, "Teknisk
+// innsikt": each query head uses its own query against the shared K/V.
+#include "launch.h"
+
+namespace kvsel {
+
+namespace {
+
+// MFMA row m of the key tile is loaded from key sigma(m): with this order the
+// 32x32x16 result tile S^T (keys x queries) leaves, in every lane, 8
+// consecutive keys per 16-key block in 8 consecutive registers - exactly the
+// B operand of the P.V MFMA, so P never leaves registers.
+__device__ __forceinline__ int sigma(int m) {
+    const int a = m >> 3, hb = (m >> 2) & 1, c = m & 3;
+    return 16 * (a >> 1) + 8 * hb + 4 * (a & 1) + c;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------- bf16 MFMA kernel
+//
+// Workgroup: 4 waves x 32 query rows; rows are (token, head-in-group) pairs,
+// row = token * G + head, so a workgroup covers 128 / G tokens of all G heads.
+// Per 64-key tile: S^T = K . Q^T (2 x KS MFMAs), online softmax on the lane's
+// query column, O^T += V^T . P^T (DB x 4 MFMAs).  K tiles are row-major
+// [key][d] and V tiles are [d][key] (written transposed by the pack kernel).
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const uint16_t* __restrict__ q,
+                                                           const uint16_t* __restrict__ kall,
+                                                           const uint16_t* __restrict__ vall,
+                                                           const int32_t* __restrict__ nsel, int nk_pad, int C, int G,
+                                                           int h_kv, int row_blocks, float cl2,
+                                                           void* __restrict__ out) {
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    constexpr int KT = 64;
+    constexpr int LDK = D + 8;
+    constexpr int LDV = KT + 8;
+    constexpr int PK = KT * D / 8 / 256;    // 16-byte K pieces per thread per tile
+    constexpr int PV = D * KT / 8 / 256;    // 16-byte V^T pieces per thread per tile
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * LDV];
+
+    const int slot = xcd_slot(blockIdx.x, gridDim.x);
+    const int bg = slot / row_blocks;
+    const int rblk = row_blocks - 1 - slot % row_blocks;      // later tokens (more keys) first
+    const int b = bg / h_kv, g = bg % h_kv;
+    const int nrows = G * C;
+    const int n_s = nsel[b];
+    const int row_wg0 = rblk * 128;
+    const int wg_tmax = min(row_wg0 + 127, nrows - 1) / G;
+    const int ntiles = (n_s + wg_tmax + 1 + KT - 1) / KT;
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int half = lane >> 5, col = lane & 31;
+    const int wrow0 = row_wg0 + wave * 32;
+    const bool wave_active = wrow0 < nrows;
+    const int w_tmin = min(wrow0, nrows - 1) / G;
+    const int w_tmax = min(wrow0 + 31, nrows - 1) / G;
+    const int qrow = wrow0 + col;
+    const bool rvalid = qrow < nrows;
+    const int tok = rvalid ? qrow / G : 0;
+    const int hh = rvalid ? qrow % G : 0;
+    const int64_t qoff = ((static_cast<int64_t>(b) * h_kv * G + g * G + hh) * C + tok) * D;
+
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (rvalid) raw = *reinterpret_cast<const u32x4*>(q + qoff + 16 * ks + 8 * half);
+        qf[ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+
+    const uint16_t* kb = kall + static_cast<int64_t>(bg) * nk_pad * D;
+    const uint16_t* vb = vall + static_cast<int64_t>(bg) * D * nk_pad;
+    u32x4 pk[PK], pv[PV];
+    auto fetch = [&](int t) {
+#pragma unroll
+        for (int i = 0; i < PK; ++i) {
+            const int p = tid + 256 * i;
+            const int r = p / (D / 8), c = p % (D / 8);
+            pk[i] = *reinterpret_cast<const u32x4*>(kb + static_cast<int64_t>(t * KT + r) * D + c * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < PV; ++i) {
+            const int p = tid + 256 * i;
+            const int d = p / (KT / 8), j = p % (KT / 8);
+            pv[i] = *reinterpret_cast<const u32x4*>(vb + static_cast<int64_t>(d) * nk_pad + t * KT + j * 8);
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < PK; ++i) {
+            const int p = tid + 256 * i;
+            const int r = p / (D / 8), c = p % (D / 8);
+            *reinterpret_cast<u32x4*>(&k_lds[buf][r * LDK + c * 8]) = pk[i];
+        }
+#pragma unroll
+        for (int i = 0; i < PV; ++i) {
+            const int p = tid + 256 * i;
+            const int d = p / (KT / 8), j = p % (KT / 8);
+            *reinterpret_cast<u32x4*>(&v_lds[buf][d * LDV + j * 8]) = pv[i];
+        }
+    };
+
+    f32x16 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+    float m = -INFINITY, l = 0.0f;
+    const int krow = sigma(col);
+    const int lim = n_s + tok;                  // last visible slot of this lane's query
+
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < ntiles) fetch(t + 1);
+        const int s0 = t * KT;
+        if (wave_active && s0 <= n_s + w_tmax) {
+            f32x16 sacc[2];
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                sacc[kb2] = f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[buf][(32 * kb2 + krow) * LDK + 16 * ks + 8 * half]);
+                    sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb2], 0, 0, 0);
+                }
+            }
+            // register r of block kb2 holds slot s0 + 32*kb2 + 16*(r>>3) + 8*half + (r&7)
+            if (s0 + KT > n_s + w_tmin) {
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int sl = s0 + 32 * kb2 + 16 * (r >> 3) + 8 * half + (r & 7);
+                        if (sl > lim) sacc[kb2][r] = -INFINITY;
+                    }
+            }
+            float mt = -INFINITY;
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb2][r]);
+            mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+            const float m_new = fmaxf(m, mt);
+            if (__ballot(m_new > m) != 0ull) {
+                const float alpha = __builtin_amdgcn_exp2f((m - m_new) * cl2);
+                l *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            }
+            m = m_new;
+            const float mc = m * cl2;
+            bf16x8 pf[2][2];
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                for (int k16 = 0; k16 < 2; ++k16) {
+                    u32x4 w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e], cl2, -mc));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e + 1], cl2, -mc));
+                        l += p0 + p1;
+                        w[e] = pack_bf16x2(p0, p1);
+                    }
+                    pf[kb2][k16] = __builtin_bit_cast(bf16x8, w);
+                }
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                    for (int k16 = 0; k16 < 2; ++k16) {
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&v_lds[buf][(32 * db + col) * LDV + 32 * kb2 + 16 * k16 + 8 * half]);
+                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb2][k16], o[db], 0, 0, 0);
+                    }
+        }
+        if (t + 1 < ntiles) stash(buf ^ 1);
+        __syncthreads();
+    }
+
+    l += __shfl_xor(l, 32, kWave);
+    if (!rvalid) return;
+    const float inv = 1.0f / l;
+    // O^T tile: register r of block db holds d = 32*db + 8*(r>>2) + 4*half + (r&3)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+            const int d0 = 32 * db + 8 * a4 + 4 * half;
+            const float v0 = o[db][4 * a4 + 0] * inv, v1 = o[db][4 * a4 + 1] * inv;
+            const float v2 = o[db][4 * a4 + 2] * inv, v3 = o[db][4 * a4 + 3] * inv;
+            if (OUT_F32) {
+                *reinterpret_cast<f32x4*>(static_cast<float*>(out) + qoff + d0) = f32x4{v0, v1, v2, v3};
+            } else {
+                uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + qoff + d0);
+                dst[0] = pack_bf16x2(v0, v1);
+                dst[1] = pack_bf16x2(v2, v3);
+            }
+        }
+}
+
+// ----------------------------------------------------------------------------- fp32 VALU kernel
+//
+// One thread per query row, key/value tiles of 32 rows staged in LDS and
+// shared by the 128 rows of the workgroup.
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(128) void attn_valu_kernel(const float* __restrict__ q, const float* __restrict__ kall,
+                                                        const float* __restrict__ vall,
+                                                        const int32_t* __restrict__ nsel, int nk_pad, int C, int G,
+                                                        int h_kv, int row_blocks, float scale,
+                                                        void* __restrict__ out) {
+    constexpr int KT = 32;
+    __shared__ float qs[128][D + 1];
+    __shared__ float kt[KT][D];
+    __shared__ float vt[KT][D];
+    const int bg = blockIdx.x / row_blocks;
+    const int rblk = row_blocks - 1 - blockIdx.x % row_blocks;
+    const int b = bg / h_kv, g = bg % h_kv;
+    const int nrows = G * C;
+    const int n_s = nsel[b];
+    const int row0 = rblk * 128;
+    const int wg_tmax = min(row0 + 127, nrows - 1) / G;
+    const int ntiles = (n_s + wg_tmax + 1 + KT - 1) / KT;
+    const int qrow = row0 + threadIdx.x;
+    const bool rvalid = qrow < nrows;
+    const int tok = rvalid ? qrow / G : 0, hh = rvalid ? qrow % G : 0;
+    const int64_t qoff = ((static_cast<int64_t>(b) * h_kv * G + g * G + hh) * C + tok) * D;
+    for (int e = 0; e < D; ++e) qs[threadIdx.x][e] = rvalid ? q[qoff + e] : 0.0f;
+    const float* kb = kall + static_cast<int64_t>(bg) * nk_pad * D;
+    const float* vb = vall + static_cast<int64_t>(bg) * nk_pad * D;
+    float acc[D];
+#pragma unroll
+    for (int e = 0; e < D; ++e) acc[e] = 0.0f;
+    float m = -INFINITY, l = 0.0f;
+    const int lim = n_s + tok;
+    for (int t = 0; t < ntiles; ++t) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < KT * D; i += 128) {
+            kt[i / D][i % D] = kb[static_cast<int64_t>(t) * KT * D + i];
+            vt[i / D][i % D] = vb[static_cast<int64_t>(t) * KT * D + i];
+        }
+        __syncthreads();
+        float s[KT];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < KT; ++j) {
+            float dot = 0.0f;
+#pragma unroll
+            for (int e = 0; e < D; ++e) dot = fmaf(qs[threadIdx.x][e], kt[j][e], dot);
+            s[j] = (t * KT + j <= lim) ? dot * scale : -INFINITY;
+            mt = fmaxf(mt, s[j]);
+        }
+        const float m_new = fmaxf(m, mt);
+        const float alpha = expf(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int e = 0; e < D; ++e) acc[e] *= alpha;
+        m = m_new;
+#pragma unroll
+        for (int j = 0; j < KT; ++j) {
+            const float p = expf(s[j] - m);
+            l += p;
+#pragma unroll
+            for (int e = 0; e < D; ++e) acc[e] = fmaf(p, vt[j][e], acc[e]);
+        }
+    }
+    if (!rvalid) return;
+    const float inv = 1.0f / l;
+    for (int e = 0; e < D; ++e) {
+        if (OUT_F32) static_cast<float*>(out)[qoff + e] = acc[e] * inv;
+        else static_cast<uint16_t*>(out)[qoff + e] = f32_to_bf16(acc[e] * inv);
+    }
+}
+
+// ----------------------------------------------------------------------------- launcher
+
+hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const void* vall, const int32_t* nsel,
+                       int nk_pad, float scale, void* out, bool out_f32, hipStream_t st) {
+    const int row_blocks = (s.G * s.C + 127) / 128;
+    dim3 grid(s.batch * s.h_kv * row_blocks);
+    if (s.esz == 2) {
+        const float cl2 = scale * 1.4426950408889634f;
+        const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)kall, *vv = (const uint16_t*)vall;
+        if (s.d == 128) {
+            if (out_f32) hipLaunchKernelGGL((attn_mfma_kernel<128, true>), grid, dim3(256), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out);
+            else hipLaunchKernelGGL((attn_mfma_kernel<128, false>), grid, dim3(256), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out);
+        } else {
+            if (out_f32) hipLaunchKernelGGL((attn_mfma_kernel<64, true>), grid, dim3(256), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out);
+            else hipLaunchKernelGGL((attn_mfma_kernel<64, false>), grid, dim3(256), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out);
+        }
+    } else {
+        const float *qq = (const float*)q, *kk = (const float*)kall, *vv = (const float*)vall;
+        if (s.d == 128) {
+            if (out_f32) hipLaunchKernelGGL((attn_valu_kernel<128, true>), grid, dim3(128), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, scale, out);
+            else hipLaunchKernelGGL((attn_valu_kernel<128, false>), grid, dim3(128), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, scale, out);
+        } else {
+            if (out_f32) hipLaunchKernelGGL((attn_valu_kernel<64, true>), grid, dim3(128), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, scale, out);
+            else hipLaunchKernelGGL((attn_valu_kernel<64, false>), grid, dim3(128), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, scale, out);
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvsel

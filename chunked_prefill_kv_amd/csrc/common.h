@@ -1,0 +1,93 @@
+// Shared device helpers for the kvsel kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvsel {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- element access
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// round-to-nearest-even fp32 -> bf16 bits (inputs are finite)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+    static constexpr int bytes = 4;
+};
+template <> struct Elem<uint16_t> {
+    static __device__ __forceinline__ float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+    static constexpr int bytes = 2;
+};
+
+// ---------------------------------------------------------------- cache addressing
+
+// Where row `pos` of sequence b, KV head g lives (contiguous or paged cache).
+struct CacheView {
+    char* k;                  // base pointers (bytes)
+    char* v;
+    int64_t capacity;         // contiguous: rows per (b, g); paged: number of blocks
+    int32_t block_size;       // 0 = contiguous
+    int32_t max_blocks;
+    const int32_t* block_table;
+    int32_t h_kv;
+    int32_t row_bytes;        // d * element bytes
+
+    __device__ __forceinline__ int64_t row_offset(int b, int g, int64_t pos) const {
+        if (block_size == 0) {
+            return ((static_cast<int64_t>(b) * h_kv + g) * capacity + pos) * row_bytes;
+        }
+        int64_t blk = block_table[static_cast<int64_t>(b) * max_blocks + pos / block_size];
+        return ((blk * h_kv + g) * block_size + pos % block_size) * static_cast<int64_t>(row_bytes);
+    }
+};
+
+// ---------------------------------------------------------------- wave helpers
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
+    return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+    return x;
+}
+
+// Order-preserving map fp32 -> uint32 (larger float -> larger key); -0 is
+// folded onto +0 first so that equal values compare equal.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The 8 workgroup-dispatch queues of MI355X place consecutive workgroup ids on
+// consecutive XCDs (each with its own L2).  remap so that the workgroups one
+// XCD receives are consecutive slots (sharing the same head's data).
+__device__ __forceinline__ int xcd_slot(int linear, int n) {
+    constexpr int kXcd = 8;
+    if (n % kXcd != 0) return linear;
+    return (linear % kXcd) * (n / kXcd) + linear / kXcd;
+}
+
+}  // namespace kvsel

@@ -1,0 +1,79 @@
+// Internal launchers of the kvsel kernels (host side).  Each returns the HIP
+// status of its launch(es).  Shapes are validated by the C-ABI layer first.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace kvsel {
+
+struct SelShape {
+    int batch, h_q, h_kv, G, d, C;   // heads, chunk length
+    int esz;                          // element bytes (2 = bf16, 4 = fp32)
+    int nqp;                          // kept queries per head = min(n_q, C)
+    int nq_pad;                       // rows reserved per head in Q_sel (>= nqp)
+    int64_t budget;
+    int64_t t_max;                    // max_b T_b
+};
+
+// Step 1: per (b, h) cosine of each chunk query to the mean query (selection
+// key) and 1/|q| of each query.  Sequences with T_b <= budget are skipped.
+hipError_t launch_qstats(const SelShape& s, const void* q, const int64_t* prior_len,
+                         float* qcos, float* qrn, hipStream_t st);
+
+// Exact top-k with lower-index tie-break, indices ascending, -1 padded to k.
+//   mode 0: the k largest of scores[p][0..n_p)      (n_p = prior_len[p / heads_per_seq])
+//   mode 1: the k smallest of scores[p][0..n_fixed) (query keep); problems
+//           whose sequence has T_b <= budget are skipped
+// When n_p <= k every index [0, n_p) is taken.
+hipError_t launch_topk(int problems, int heads_per_seq, const float* scores, int64_t score_stride,
+                       const int64_t* prior_len, int n_fixed, int64_t budget, int k,
+                       int32_t* out, int64_t out_stride, int mode, hipStream_t st);
+
+// Gather the kept query rows of every head into Q_sel[b][g][hh*nq_pad + r][d]
+// (raw rows) and rq = 1/|q|; rows r >= nqp repeat row 0 of that head.
+hipError_t launch_pack_qsel(const SelShape& s, const void* q, const int32_t* keep, int64_t keep_stride,
+                            const float* qrn, const int64_t* prior_len, void* qsel, float* rq,
+                            hipStream_t st);
+
+// Step 2: S[b][g][j] for j < T_b (sequences with T_b > budget only).
+hipError_t launch_scan(const SelShape& s, const void* qsel, const float* rq, const CacheView& cv,
+                       const int64_t* prior_len, float* S, int64_t s_stride, hipStream_t st);
+
+// Step 4 for the select API: k_sel[b][g][r] = cache row idx[b][g][r], r < min(budget, T_b).
+hipError_t launch_gather(const SelShape& s, const CacheView& cv, const int64_t* prior_len,
+                         const int32_t* idx, int64_t idx_stride, void* k_sel, void* v_sel,
+                         hipStream_t st);
+
+// Compacted key/value layout consumed by the attention kernels:
+//   kall [b][g][nk_pad][d]; vall [b][g][d][nk_pad] (bf16, transposed) or
+//   [b][g][nk_pad][d] (fp32).  Slot s < nsel_b: prior key, s < nsel_b + C: the
+//   chunk's key s - nsel_b, beyond: zeros.
+struct PackSrc {
+    // prior keys from the cache through idx (compact == nullptr) ...
+    const CacheView* cache;
+    const int64_t* prior_len;
+    int64_t budget;
+    const int32_t* idx;
+    int64_t idx_stride;
+    // ... or from a caller-supplied compacted array [b][g][n_sel_max][d]
+    const void* k_compact;
+    const void* v_compact;
+    const int32_t* n_sel;
+    int n_sel_max;
+};
+hipError_t launch_pack(const SelShape& s, const PackSrc& src, const void* k_chunk, const void* v_chunk,
+                       int nk_pad, void* kall, void* vall, int32_t* nsel_out, hipStream_t st);
+
+// Step 5 over the packed layout; out is fp32 (out_f32) or bf16.
+hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const void* vall,
+                       const int32_t* nsel, int nk_pad, float scale, void* out, bool out_f32,
+                       hipStream_t st);
+
+// Append the chunk's K/V rows at [T_b, T_b + C).
+hipError_t launch_append(const SelShape& s, const CacheView& cv, const int64_t* prior_len,
+                         const void* k_chunk, const void* v_chunk, hipStream_t st);
+
+}  // namespace kvsel

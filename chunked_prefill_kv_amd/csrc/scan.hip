@@ -1,0 +1,321 @@
+// Key-scoring scan over the whole prior cache.
+//
+// QuoKA article ("Qualcomm QuoKA", itsolotime.com), Fig. 1(b) and the method
+// paragraph: each cache key is scored by its cosine similarity with the kept
+// queries, max-pooled over the queries of a head and mean-pooled over the
+// query heads that share the KV head (GQA):
+//   S[g][j] = (1/G) * sum_h max_i (q_{h,i} . k_j) / (|q_{h,i}| |k_j|)
+// The raw bf16 products are accumulated in fp32 by MFMA and scaled by the
+// fp32 reciprocal norms afterwards (normalised vectors are never rounded to
+// bf16); 1/|k_j| is common to every query so it is applied after the max.
+#include "launch.h"
+
+namespace kvsel {
+
+// ----------------------------------------------------------------------------- prefill scan (MFMA 32x32x16)
+//
+// Workgroup = 4 waves x NB blocks of 32 keys.  Each wave keeps its keys'
+// bf16 fragments in registers for the whole kernel (the B operand, loaded from
+// HBM exactly once) and streams the packed kept queries Q_sel (the A operand,
+// G * nq_pad rows, L2-resident) through a double-buffered LDS stage.  The
+// MFMA result tile has queries on rows and keys on columns, so each lane holds
+// 16 query rows of one key: the max over queries is in-register plus one
+// exchange between the two half-waves at the end of every head.
+template <int D, int NB>
+__global__ __launch_bounds__(256, 2) void scan_mfma_kernel(const uint16_t* __restrict__ qsel,
+                                                           const float* __restrict__ rq, CacheView cv,
+                                                           const int64_t* __restrict__ prior_len, int64_t budget,
+                                                           int h_kv, int G, int nq_pad, int tiles,
+                                                           float* __restrict__ S, int64_t s_stride) {
+    constexpr int KS = D / 16;              // MFMA k-steps over the head dim
+    constexpr int KEYS = 4 * NB * 32;       // keys per workgroup
+    constexpr int STAGE = 64;               // query rows per LDS stage
+    constexpr int LDQ = D + 8;              // padded LDS row (bf16 elements)
+    constexpr int PIECES = STAGE * D / 8;   // 16-byte pieces per stage
+    constexpr int PPT = PIECES / 256;       // pieces per thread
+    __shared__ __attribute__((aligned(16))) uint16_t qs[2][STAGE * LDQ];
+    __shared__ __attribute__((aligned(16))) float rqs[2][STAGE];
+
+    const int slot = xcd_slot(blockIdx.x, gridDim.x);
+    const int bg = slot / tiles, tile = slot % tiles;
+    const int b = bg / h_kv, g = bg % h_kv;
+    const int64_t T = prior_len[b];
+    if (T <= budget) return;
+    const int64_t key0 = static_cast<int64_t>(tile) * KEYS;
+    if (key0 >= T) return;
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int half = lane >> 5, col = lane & 31;
+
+    // ---- this wave's keys: fragments + reciprocal norms
+    bf16x8 kf[NB][KS];
+    float rk[NB];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+        const int64_t key = key0 + (wave * NB + kb) * 32 + col;
+        const bool valid = key < T;
+        const char* row = cv.k + (valid ? cv.row_offset(b, g, key) : 0);
+        float n2 = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (valid) raw = *reinterpret_cast<const u32x4*>(row + (16 * ks + 8 * half) * 2);
+            kf[kb][ks] = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo = __uint_as_float(raw[i] << 16), hi = __uint_as_float(raw[i] & 0xFFFF0000u);
+                n2 = fmaf(lo, lo, n2);
+                n2 = fmaf(hi, hi, n2);
+            }
+        }
+        n2 += __shfl_xor(n2, 32, kWave);
+        rk[kb] = n2 > 0.0f ? 1.0f / sqrtf(n2) : 0.0f;
+    }
+
+    const int R = G * nq_pad;
+    const int nstage = (R + STAGE - 1) / STAGE;
+    const uint16_t* qb = qsel + static_cast<int64_t>(bg) * R * D;
+    const float* rqb = rq + static_cast<int64_t>(bg) * R;
+
+    u32x4 pre[PPT];
+    float prq = 0.0f;
+    auto fetch = [&](int s) {
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int p = tid + 256 * i;
+            const int r = p / (D / 8), c8 = p % (D / 8);
+            const int row = s * STAGE + r;
+            pre[i] = row < R ? *reinterpret_cast<const u32x4*>(qb + static_cast<int64_t>(row) * D + c8 * 8)
+                             : u32x4{0u, 0u, 0u, 0u};
+        }
+        if (tid < STAGE) {
+            const int row = s * STAGE + tid;
+            prq = row < R ? rqb[row] : 0.0f;
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int p = tid + 256 * i;
+            const int r = p / (D / 8), c8 = p % (D / 8);
+            *reinterpret_cast<u32x4*>(&qs[buf][r * LDQ + c8 * 8]) = pre[i];
+        }
+        if (tid < STAGE) rqs[buf][tid] = prq;
+    };
+
+    float run[NB], sum[NB];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) { run[kb] = -INFINITY; sum[kb] = 0.0f; }
+
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int s = 0; s < nstage; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < nstage) fetch(s + 1);
+#pragma unroll
+        for (int rb = 0; rb < STAGE / 32; ++rb) {
+            const int row0 = s * STAGE + rb * 32;
+            if (row0 < R) {
+                bf16x8 a[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    a[ks] = *reinterpret_cast<const bf16x8*>(&qs[buf][(rb * 32 + col) * LDQ + 16 * ks + 8 * half]);
+                float rv[16];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(&rqs[buf][rb * 32 + 8 * q4 + 4 * half]);
+                    rv[4 * q4 + 0] = v[0]; rv[4 * q4 + 1] = v[1]; rv[4 * q4 + 2] = v[2]; rv[4 * q4 + 3] = v[3];
+                }
+#pragma unroll
+                for (int kb = 0; kb < NB; ++kb) {
+                    f32x16 acc = {};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], kf[kb][ks], acc, 0, 0, 0);
+                    float m = run[kb];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[r] * rv[r]);
+                    run[kb] = m;
+                }
+                if ((row0 + 32) % nq_pad == 0) {      // last 32-row block of a head
+#pragma unroll
+                    for (int kb = 0; kb < NB; ++kb) {
+                        const float m = fmaxf(run[kb], __shfl_xor(run[kb], 32, kWave));
+                        sum[kb] += m;
+                        run[kb] = -INFINITY;
+                    }
+                }
+            }
+        }
+        if (s + 1 < nstage) stash(buf ^ 1);
+        __syncthreads();
+    }
+
+    const float inv_g = 1.0f / static_cast<float>(G);
+    float* Sb = S + static_cast<int64_t>(bg) * s_stride;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+        const int64_t key = key0 + (wave * NB + kb) * 32 + col;
+        if (half == 0 && key < T) Sb[key] = sum[kb] * inv_g * rk[kb];
+    }
+}
+
+// ----------------------------------------------------------------------------- one kept query per head (MFMA 16x16x32)
+//
+// With a single query per head (decode, or N_q = 1) the G <= 16 query heads of
+// a KV head form the 16 rows of one MFMA tile; keys stream through registers
+// straight from HBM (this scan is bandwidth-bound: 4 useful rows per key).
+template <int D>
+__global__ __launch_bounds__(256) void scan_rows16_kernel(const uint16_t* __restrict__ qsel,
+                                                         const float* __restrict__ rq, CacheView cv,
+                                                         const int64_t* __restrict__ prior_len, int64_t budget,
+                                                         int h_kv, int G, int tiles, float* __restrict__ S,
+                                                         int64_t s_stride) {
+    constexpr int KS = D / 32;          // k-steps of 32
+    constexpr int GROUPS = 4;           // 16-key groups per wave
+    constexpr int KEYS = 4 * GROUPS * 16;
+    const int slot = xcd_slot(blockIdx.x, gridDim.x);
+    const int bg = slot / tiles, tile = slot % tiles;
+    const int b = bg / h_kv, g = bg % h_kv;
+    const int64_t T = prior_len[b];
+    if (T <= budget) return;
+    const int64_t key0 = static_cast<int64_t>(tile) * KEYS;
+    if (key0 >= T) return;
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int quad = lane >> 4, col = lane & 15;
+
+    // A: query rows (row m = query head m of the group, zero past G)
+    bf16x8 a[KS];
+    {
+        const bool valid = col < G;
+        const uint16_t* qrow = qsel + (static_cast<int64_t>(bg) * G + (valid ? col : 0)) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (valid) raw = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * quad);
+            a[ks] = __builtin_bit_cast(bf16x8, raw);
+        }
+    }
+    float rv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = 4 * quad + r;
+        rv[r] = row < G ? rq[static_cast<int64_t>(bg) * G + row] : 0.0f;
+    }
+
+    u32x4 raw[GROUPS][KS];
+#pragma unroll
+    for (int gr = 0; gr < GROUPS; ++gr) {
+        const int64_t key = key0 + wave * GROUPS * 16 + gr * 16 + col;
+        const bool valid = key < T;
+        const char* row = cv.k + (valid ? cv.row_offset(b, g, key) : 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            raw[gr][ks] = valid ? *reinterpret_cast<const u32x4*>(row + (32 * ks + 8 * quad) * 2) : u32x4{0u, 0u, 0u, 0u};
+    }
+    const float inv_g = 1.0f / static_cast<float>(G);
+    float* Sb = S + static_cast<int64_t>(bg) * s_stride;
+#pragma unroll
+    for (int gr = 0; gr < GROUPS; ++gr) {
+        f32x4 acc = {};
+        float n2 = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], __builtin_bit_cast(bf16x8, raw[gr][ks]), acc, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo = __uint_as_float(raw[gr][ks][i] << 16), hi = __uint_as_float(raw[gr][ks][i] & 0xFFFF0000u);
+                n2 = fmaf(lo, lo, n2);
+                n2 = fmaf(hi, hi, n2);
+            }
+        }
+        float v = acc[0] * rv[0] + acc[1] * rv[1] + acc[2] * rv[2] + acc[3] * rv[3];
+        v += __shfl_xor(v, 16, kWave);
+        v += __shfl_xor(v, 32, kWave);
+        n2 += __shfl_xor(n2, 16, kWave);
+        n2 += __shfl_xor(n2, 32, kWave);
+        const float rkv = n2 > 0.0f ? 1.0f / sqrtf(n2) : 0.0f;
+        const int64_t key = key0 + wave * GROUPS * 16 + gr * 16 + col;
+        if (quad == 0 && key < T) Sb[key] = v * inv_g * rkv;
+    }
+}
+
+// ----------------------------------------------------------------------------- generic VALU scan (fp32 inputs)
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void scan_valu_kernel(const E* __restrict__ qsel, const float* __restrict__ rq,
+                                                        CacheView cv, const int64_t* __restrict__ prior_len,
+                                                        int64_t budget, int h_kv, int G, int nqp, int tiles,
+                                                        float* __restrict__ S, int64_t s_stride) {
+    constexpr int QR = 32;
+    __shared__ float qs[QR][D];
+    __shared__ float rqs[QR];
+    const int bg = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+    const int b = bg / h_kv, g = bg % h_kv;
+    const int64_t T = prior_len[b];
+    if (T <= budget) return;
+    const int64_t key0 = static_cast<int64_t>(tile) * 256;
+    if (key0 >= T) return;
+    const int64_t key = key0 + threadIdx.x;
+    const bool valid = key < T;
+    float k[D];
+    {
+        const E* row = reinterpret_cast<const E*>(cv.k + (valid ? cv.row_offset(b, g, key) : 0));
+#pragma unroll
+        for (int e = 0; e < D; ++e) k[e] = valid ? Elem<E>::load(row, e) : 0.0f;
+    }
+    float n2 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < D; ++e) n2 = fmaf(k[e], k[e], n2);
+    const float rkv = n2 > 0.0f ? 1.0f / sqrtf(n2) : 0.0f;
+    const E* qb = qsel + static_cast<int64_t>(bg) * G * nqp * D;
+    const float* rqb = rq + static_cast<int64_t>(bg) * G * nqp;
+    float sum = 0.0f;
+    for (int hh = 0; hh < G; ++hh) {
+        float run = -INFINITY;
+        for (int r0 = 0; r0 < nqp; r0 += QR) {
+            const int nr = min(QR, nqp - r0);
+            __syncthreads();
+            for (int i = threadIdx.x; i < nr * D; i += 256)
+                qs[i / D][i % D] = Elem<E>::load(qb, (static_cast<int64_t>(hh) * nqp + r0) * D + i);
+            if (threadIdx.x < nr) rqs[threadIdx.x] = rqb[hh * nqp + r0 + threadIdx.x];
+            __syncthreads();
+            for (int r = 0; r < nr; ++r) {
+                float dot = 0.0f;
+#pragma unroll
+                for (int e = 0; e < D; ++e) dot = fmaf(qs[r][e], k[e], dot);
+                run = fmaxf(run, dot * rqs[r]);
+            }
+        }
+        sum += run;
+    }
+    if (valid) S[static_cast<int64_t>(bg) * s_stride + key] = sum * (1.0f / static_cast<float>(G)) * rkv;
+}
+
+// ----------------------------------------------------------------------------- launcher
+
+hipError_t launch_scan(const SelShape& s, const void* qsel, const float* rq, const CacheView& cv,
+                       const int64_t* prior_len, float* S, int64_t s_stride, hipStream_t st) {
+    const int bgs = s.batch * s.h_kv;
+    if (s.esz == 2 && s.nq_pad == 1) {          // one query per head, G <= 16
+        const int tiles = static_cast<int>((s.t_max + 255) / 256);
+        dim3 grid(bgs * tiles), block(256);
+        if (s.d == 128) hipLaunchKernelGGL((scan_rows16_kernel<128>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride);
+        else hipLaunchKernelGGL((scan_rows16_kernel<64>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride);
+    } else if (s.esz == 2) {
+        constexpr int NB = 2;
+        const int tiles = static_cast<int>((s.t_max + 4 * NB * 32 - 1) / (4 * NB * 32));
+        dim3 grid(bgs * tiles), block(256);
+        if (s.d == 128) hipLaunchKernelGGL((scan_mfma_kernel<128, NB>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, S, s_stride);
+        else hipLaunchKernelGGL((scan_mfma_kernel<64, NB>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, S, s_stride);
+    } else {
+        const int tiles = static_cast<int>((s.t_max + 255) / 256);
+        dim3 grid(bgs * tiles), block(256);
+        if (s.d == 128) hipLaunchKernelGGL((scan_valu_kernel<float, 128>), grid, block, 0, st, (const float*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, S, s_stride);
+        else hipLaunchKernelGGL((scan_valu_kernel<float, 64>), grid, block, 0, st, (const float*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, S, s_stride);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvsel

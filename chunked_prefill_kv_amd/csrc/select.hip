@@ -1,0 +1,298 @@
+// Query sub-selection statistics, exact radix top-k, and Q_sel packing.
+//
+// QuoKA article ("Qualcomm QuoKA", itsolotime.com), Fig. 1(b) and Fig. 2:
+// queries are filtered by their cosine dissimilarity to the chunk's mean
+// query (high S_q = low cosine kept); Fig. 1(a): the best-scoring keys of the
+// cache are kept.  Both selections here are exact (no bucketing): a radix
+// select finds the k-th key, ties go to the lower index, and the kept indices
+// are written in ascending order.
+#include "launch.h"
+
+namespace kvsel {
+
+// ----------------------------------------------------------------------------- helpers
+
+template <typename T> struct Vec8;
+template <> struct Vec8<uint16_t> {   // 8 bf16 = one 16-byte load
+    static __device__ __forceinline__ void load(const uint16_t* p, float* out) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(v[i] << 16);
+            out[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+        }
+    }
+};
+template <> struct Vec8<float> {      // 8 fp32 = two 16-byte loads
+    static __device__ __forceinline__ void load(const float* p, float* out) {
+        f32x4 a = *reinterpret_cast<const f32x4*>(p);
+        f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { out[i] = a[i]; out[4 + i] = b[i]; }
+    }
+};
+
+// ----------------------------------------------------------------------------- step 1 statistics
+
+// One workgroup per (sequence, query head).  The mean query and every dot
+// product / norm are accumulated in fp64 (the inputs are exact in fp32), so
+// the selection key carries only the final fp32 rounding.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void qstats_kernel(const T* __restrict__ q, int h_q, int C,
+                                                     const int64_t* __restrict__ prior_len, int64_t budget,
+                                                     float* __restrict__ qcos, float* __restrict__ qrn) {
+    const int bh = blockIdx.x;
+    const int b = bh / h_q;
+    if (prior_len[b] <= budget) return;
+    const T* qh = q + static_cast<int64_t>(bh) * C * D;
+    constexpr int kSub = 256 / D;
+    __shared__ double part[kSub][D];
+    __shared__ double mean[D];
+    __shared__ double mnorm;
+    const int c = threadIdx.x % D, sub = threadIdx.x / D;
+    double acc = 0.0;
+    for (int r = sub; r < C; r += kSub) acc += static_cast<double>(Elem<T>::load(qh, static_cast<int64_t>(r) * D + c));
+    part[sub][c] = acc;
+    __syncthreads();
+    if (threadIdx.x < D) {
+        double s = 0.0;
+#pragma unroll
+        for (int k = 0; k < kSub; ++k) s += part[k][threadIdx.x];
+        mean[threadIdx.x] = s / C;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double s = 0.0;
+        for (int e = 0; e < D; ++e) s += mean[e] * mean[e];
+        mnorm = sqrt(s);
+    }
+    __syncthreads();
+    const double mn = mnorm;
+    for (int r = threadIdx.x; r < C; r += 256) {
+        const T* row = qh + static_cast<int64_t>(r) * D;
+        double dot = 0.0, n2 = 0.0;
+#pragma unroll 2
+        for (int e0 = 0; e0 < D; e0 += 8) {
+            float x[8];
+            Vec8<T>::load(row + e0, x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const double xd = x[i];
+                dot += xd * mean[e0 + i];
+                n2 += xd * xd;
+            }
+        }
+        const double nq = sqrt(n2);
+        const double den = nq * mn;
+        qcos[static_cast<int64_t>(bh) * C + r] = den > 0.0 ? static_cast<float>(dot / den) : 0.0f;
+        qrn[static_cast<int64_t>(bh) * C + r] = nq > 0.0 ? static_cast<float>(1.0 / nq) : 0.0f;
+    }
+}
+
+// ----------------------------------------------------------------------------- exact top-k
+
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / kWave;
+constexpr int kHistBins = 2048;   // 11-bit digits
+
+// Exclusive scan of one uint32 per thread across the workgroup (ascending thread id).
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    uint32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        uint32_t t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+    }
+    if (lane == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) {
+        const uint32_t s = wsum[w];
+        off += (w < wave) ? s : 0u;
+        tot += s;
+    }
+    __syncthreads();
+    *total = tot;
+    return off + incl - v;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores, int64_t score_stride,
+                                                            int heads_per_seq, const int64_t* __restrict__ prior_len,
+                                                            int n_fixed, int64_t budget, int k,
+                                                            int32_t* __restrict__ out, int64_t out_stride, int mode) {
+    const int p = blockIdx.x;
+    const int b = p / heads_per_seq;
+    const int64_t T = prior_len[b];
+    int n;
+    if (mode == 0) {
+        n = static_cast<int>(T);
+    } else {
+        if (T <= budget) return;
+        n = n_fixed;
+    }
+    const float* x = scores + static_cast<int64_t>(p) * score_stride;
+    int32_t* o = out + static_cast<int64_t>(p) * out_stride;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+
+    if (n <= k) {   // everything is kept
+        for (int j = tid; j < k; j += kTopkThreads) o[j] = j < n ? j : -1;
+        return;
+    }
+    const uint32_t flip = mode ? 0xFFFFFFFFu : 0u;   // mode 1 keeps the smallest
+    auto key = [&](int j) -> uint32_t { return order_key(x[j]) ^ flip; };
+
+    __shared__ uint32_t hist[kHistBins];
+    __shared__ uint32_t wsum[kTopkWaves];
+    __shared__ uint32_t wtot[2][kTopkWaves];
+    __shared__ uint32_t s_digit, s_rem;
+
+    // bits shared by every key need no histogram pass
+    const uint32_t first = key(0);
+    uint32_t diff = 0;
+    for (int j = tid; j < n; j += kTopkThreads) diff |= key(j) ^ first;
+#pragma unroll
+    for (int o2 = 32; o2 >= 1; o2 >>= 1) diff |= __shfl_xor(diff, o2, kWave);
+    if (lane == 0) wsum[wave] = diff;
+    __syncthreads();
+    diff = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) diff |= wsum[w];
+    __syncthreads();
+
+    int bits = diff ? 32 - __clz(diff) : 0;        // low bits still unresolved
+    uint32_t prefix = bits == 32 ? 0u : (first >> bits) << bits;
+    uint32_t remaining = static_cast<uint32_t>(k);
+    while (bits > 0) {
+        const int w = bits < 11 ? bits : 11;
+        const int shift = bits - w;
+        const uint32_t dmask = (1u << w) - 1u;
+        for (int i = tid; i < kHistBins; i += kTopkThreads) hist[i] = 0;
+        __syncthreads();
+        for (int j = tid; j < n; j += kTopkThreads) {
+            const uint32_t u = key(j);
+            const bool match = (bits == 32) || ((u >> bits) == (prefix >> bits));
+            if (match) atomicAdd(&hist[(u >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        // thread t owns bins 2t, 2t+1; counts of all higher bins via a reversed scan
+        const int t = kTopkThreads - 1 - tid;               // reversed order
+        const uint32_t h0 = hist[2 * t], h1 = hist[2 * t + 1];
+        uint32_t tot;
+        const uint32_t above = block_excl_scan(h0 + h1, wsum, &tot);   // bins > 2t+1
+        if (above < remaining && above + h1 >= remaining) {
+            s_digit = 2 * t + 1;
+            s_rem = remaining - above;
+        } else if (above + h1 < remaining && above + h1 + h0 >= remaining) {
+            s_digit = 2 * t;
+            s_rem = remaining - above - h1;
+        }
+        __syncthreads();
+        prefix |= s_digit << shift;
+        remaining = s_rem;
+        bits = shift;
+        __syncthreads();
+    }
+    const uint32_t tau = prefix;          // the k-th largest key
+    const uint32_t need = remaining;      // keys equal to tau that are kept (lowest indices)
+
+    const uint64_t lt = (1ull << lane) - 1ull;
+    uint32_t eq_before = 0, sel_before = 0;
+    for (int base = 0; base < n && sel_before < static_cast<uint32_t>(k); base += kTopkThreads) {
+        const int j = base + tid;
+        const uint32_t u = j < n ? key(j) : 0u;
+        const bool gt = j < n && u > tau;
+        const bool eq = j < n && u == tau;
+        const uint64_t be = __ballot(eq);
+        if (lane == 0) wtot[0][wave] = __popcll(be);
+        __syncthreads();
+        uint32_t off_eq = 0, tot_eq = 0;
+#pragma unroll
+        for (int w = 0; w < kTopkWaves; ++w) {
+            const uint32_t s = wtot[0][w];
+            off_eq += (w < wave) ? s : 0u;
+            tot_eq += s;
+        }
+        const uint32_t eq_rank = eq_before + off_eq + __popcll(be & lt);
+        const bool sel = gt || (eq && eq_rank < need);
+        const uint64_t bs = __ballot(sel);
+        if (lane == 0) wtot[1][wave] = __popcll(bs);
+        __syncthreads();
+        uint32_t off_sel = 0, tot_sel = 0;
+#pragma unroll
+        for (int w = 0; w < kTopkWaves; ++w) {
+            const uint32_t s = wtot[1][w];
+            off_sel += (w < wave) ? s : 0u;
+            tot_sel += s;
+        }
+        if (sel) o[sel_before + off_sel + __popcll(bs & lt)] = j;
+        eq_before += tot_eq;
+        sel_before += tot_sel;
+        __syncthreads();
+    }
+}
+
+// ----------------------------------------------------------------------------- Q_sel packing
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pack_qsel_kernel(const T* __restrict__ q, int h_q, int G, int C, int nqp,
+                                                        int nq_pad, const int32_t* __restrict__ keep,
+                                                        int64_t keep_stride, const float* __restrict__ qrn,
+                                                        const int64_t* __restrict__ prior_len, int64_t budget,
+                                                        T* __restrict__ qsel, float* __restrict__ rq) {
+    const int bh = blockIdx.x;
+    const int b = bh / h_q, h = bh % h_q;
+    if (prior_len[b] <= budget) return;
+    const int g = h / G, hh = h % G;
+    const int h_kv = h_q / G;
+    constexpr int kPieces = D * sizeof(T) / 16;          // 16-byte pieces per row
+    const int64_t dst_row0 = (static_cast<int64_t>(b) * h_kv + g) * G * nq_pad + static_cast<int64_t>(hh) * nq_pad;
+    const int32_t* kp = keep + static_cast<int64_t>(bh) * keep_stride;
+    for (int i = threadIdx.x; i < nq_pad * kPieces; i += 256) {
+        const int r = i / kPieces, pc = i % kPieces;
+        const int t = kp[r < nqp ? r : 0];
+        const u32x4* src = reinterpret_cast<const u32x4*>(q + (static_cast<int64_t>(bh) * C + t) * D) + pc;
+        u32x4* dst = reinterpret_cast<u32x4*>(qsel + (dst_row0 + r) * D) + pc;
+        *dst = *src;
+        if (pc == 0) rq[dst_row0 + r] = qrn[static_cast<int64_t>(bh) * C + t];
+    }
+}
+
+// ----------------------------------------------------------------------------- launchers
+
+hipError_t launch_qstats(const SelShape& s, const void* q, const int64_t* prior_len, float* qcos, float* qrn,
+                         hipStream_t st) {
+    dim3 grid(s.batch * s.h_q), block(256);
+    if (s.esz == 2) {
+        if (s.d == 128) hipLaunchKernelGGL((qstats_kernel<uint16_t, 128>), grid, block, 0, st, (const uint16_t*)q, s.h_q, s.C, prior_len, s.budget, qcos, qrn);
+        else hipLaunchKernelGGL((qstats_kernel<uint16_t, 64>), grid, block, 0, st, (const uint16_t*)q, s.h_q, s.C, prior_len, s.budget, qcos, qrn);
+    } else {
+        if (s.d == 128) hipLaunchKernelGGL((qstats_kernel<float, 128>), grid, block, 0, st, (const float*)q, s.h_q, s.C, prior_len, s.budget, qcos, qrn);
+        else hipLaunchKernelGGL((qstats_kernel<float, 64>), grid, block, 0, st, (const float*)q, s.h_q, s.C, prior_len, s.budget, qcos, qrn);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(int problems, int heads_per_seq, const float* scores, int64_t score_stride,
+                       const int64_t* prior_len, int n_fixed, int64_t budget, int k, int32_t* out,
+                       int64_t out_stride, int mode, hipStream_t st) {
+    hipLaunchKernelGGL(topk_kernel, dim3(problems), dim3(kTopkThreads), 0, st, scores, score_stride, heads_per_seq,
+                       prior_len, n_fixed, budget, k, out, out_stride, mode);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_qsel(const SelShape& s, const void* q, const int32_t* keep, int64_t keep_stride,
+                            const float* qrn, const int64_t* prior_len, void* qsel, float* rq, hipStream_t st) {
+    dim3 grid(s.batch * s.h_q), block(256);
+    if (s.esz == 2) {
+        if (s.d == 128) hipLaunchKernelGGL((pack_qsel_kernel<uint16_t, 128>), grid, block, 0, st, (const uint16_t*)q, s.h_q, s.G, s.C, s.nqp, s.nq_pad, keep, keep_stride, qrn, prior_len, s.budget, (uint16_t*)qsel, rq);
+        else hipLaunchKernelGGL((pack_qsel_kernel<uint16_t, 64>), grid, block, 0, st, (const uint16_t*)q, s.h_q, s.G, s.C, s.nqp, s.nq_pad, keep, keep_stride, qrn, prior_len, s.budget, (uint16_t*)qsel, rq);
+    } else {
+        if (s.d == 128) hipLaunchKernelGGL((pack_qsel_kernel<float, 128>), grid, block, 0, st, (const float*)q, s.h_q, s.G, s.C, s.nqp, s.nq_pad, keep, keep_stride, qrn, prior_len, s.budget, (float*)qsel, rq);
+        else hipLaunchKernelGGL((pack_qsel_kernel<float, 64>), grid, block, 0, st, (const float*)q, s.h_q, s.G, s.C, s.nqp, s.nq_pad, keep, keep_stride, qrn, prior_len, s.budget, (float*)qsel, rq);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvsel

@@ -1,0 +1,164 @@
+/*
+ * kvsel.h - query-oriented KV selection (QuoKA) + compacted attention for
+ * chunked prefill, as a C ABI over hand-written gfx950 (MI355X) HIP kernels.
+ *
+ * What is computed (QuoKA article, "Qualcomm QuoKA", itsolotime.com, Fig. 1(a)
+ * and 1(b) and the method paragraph after Fig. 1): a prompt is processed one
+ * chunk at a time; for each chunk of C queries at positions [T, T+C)
+ *   1. per query head h, the chunk's mean query m_h is formed and the n_q
+ *      queries with the smallest cosine to m_h are kept (ties: lower token);
+ *   2. every prior cache key j < T of KV head g is scored
+ *      S[g][j] = mean over the G = h_q / h_kv query heads h of g of
+ *                max over kept queries i of h of cos(q_{h,i}, k_{g,j});
+ *   3. the `budget` highest-scoring keys are kept per KV head (ties: lower
+ *      index; indices reported ascending); when T <= budget every prior key
+ *      is kept and steps 1-2 are skipped;
+ *   4. the kept K/V rows are compacted and
+ *   5. every chunk query attends, with softmax scale 1/sqrt(d) (or `scale`),
+ *      to the compacted prior keys (all visible) plus the chunk's own keys
+ *      under the causal mask; KV head of query head h is h / G (grouped and
+ *      multi-query attention, multi-query attention page, "Teknisk innsikt").
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers unless marked [host].  The caller owns all
+ *     device memory, including the workspace; the library allocates nothing
+ *     and keeps no per-call state.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on it and returns without synchronising.
+ *   - Arguments are checked on the host before anything is enqueued; on an
+ *     error the call returns a non-zero kvsel_status with nothing enqueued and
+ *     kvsel_last_error() describes it.  A failed launch returns
+ *     KVSEL_ERR_HIP.  Errors during execution surface at the caller's next
+ *     synchronisation.  No C++ exception crosses this boundary.
+ *   - Tensors are dense row-major with the shapes given; element type is
+ *     `heads->dtype` for q/k/v (fp32 or bf16 bit patterns), accumulation is
+ *     always fp32.
+ *   - The same inputs give bitwise-identical outputs (no floating-point
+ *     atomics anywhere).
+ */
+#ifndef KVSEL_H
+#define KVSEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVSEL_OK = 0,
+    KVSEL_ERR_INVALID_ARG = 1,   /* a null pointer, a bad shape, an out-of-range value */
+    KVSEL_ERR_UNSUPPORTED = 2,   /* a valid request this build does not implement (e.g. d = 96) */
+    KVSEL_ERR_WORKSPACE = 3,     /* workspace missing or smaller than kvsel_workspace_size() */
+    KVSEL_ERR_HIP = 4            /* a HIP launch failed; kvsel_last_error() has the HIP message */
+} kvsel_status;
+
+typedef enum { KVSEL_F32 = 0, KVSEL_BF16 = 1 } kvsel_dtype;
+
+/* Attention heads of one layer.  h_q % h_kv == 0; d in {64, 128};
+ * scale == 0 means 1/sqrt(d). */
+typedef struct {
+    int32_t h_q, h_kv, d;
+    int32_t dtype;               /* kvsel_dtype of q, k, v */
+    float scale;
+} kvsel_heads;
+
+/* Selection budget.  n_q >= 1 queries kept per query head (all when
+ * n_q >= chunk_len); budget >= 1 prior keys kept per KV head. */
+typedef struct {
+    int32_t n_q, budget;
+} kvsel_params;
+
+/* One layer's KV cache.
+ *   contiguous (block_size == 0): k, v are [batch][h_kv][capacity][d]; the
+ *     prior tokens of sequence b are rows [0, T_b).
+ *   paged (block_size > 0): k, v are [capacity][h_kv][block_size][d]
+ *     (capacity = number of physical blocks); position p of sequence b lives
+ *     in block block_table[b * max_blocks_per_seq + p / block_size], row
+ *     p % block_size.  Every block a call touches must be mapped. */
+typedef struct {
+    void *k, *v;
+    int64_t capacity;
+    int32_t block_size;
+    int32_t max_blocks_per_seq;
+    const int32_t *block_table;  /* paged only: [batch][max_blocks_per_seq] */
+} kvsel_cache;
+
+/* The sequences of one call.  Every sequence contributes chunk_len new tokens
+ * (chunk_len == 1 is a decode step). */
+typedef struct {
+    int32_t batch, chunk_len;
+    const int64_t *prior_len_host;   /* [host][batch] T_b: sizes the grids, no device->host copy */
+    const int64_t *prior_len_dev;    /* [batch] the same values in device memory */
+} kvsel_batch;
+
+/* Workspace bytes that kvsel_select and kvsel_prefill_chunk need for these
+ * shapes (the larger of the two).  Writes *bytes; returns a status. */
+kvsel_status kvsel_workspace_size(const kvsel_heads *heads, const kvsel_batch *batch,
+                                  const kvsel_params *params, size_t *bytes);
+
+/* Workspace bytes that kvsel_sparse_attn needs. */
+kvsel_status kvsel_sparse_attn_workspace_size(const kvsel_heads *heads, const kvsel_batch *batch,
+                                              int32_t n_sel_max, size_t *bytes);
+
+/* Steps 1-3 (and the compaction of step 4 when k_sel/v_sel are given) for one
+ * chunk of every sequence, against the prior cache rows [0, T_b).
+ *   q       [batch][h_q][chunk_len][d]
+ *   cache   read only
+ *   idx     out [batch][h_kv][budget] int32: kept prior positions, ascending,
+ *           -1 past min(budget, T_b)
+ *   k_sel, v_sel  optional out [batch][h_kv][budget][d]: the kept rows, copied
+ *           bit for bit; rows past min(budget, T_b) are not written.  Both or
+ *           neither.
+ *   q_keep  optional debug out [batch][h_q][min(n_q, chunk_len)] int32: the
+ *           kept query tokens, ascending; written only for sequences with
+ *           T_b > budget.
+ *   scores  optional debug out [batch][h_kv][score_stride] fp32 with
+ *           score_stride = max_b T_b: S[g][j] for j < T_b; written only for
+ *           sequences with T_b > budget. */
+kvsel_status kvsel_select(const kvsel_heads *heads, const kvsel_batch *batch,
+                          const kvsel_params *params, const void *q, const kvsel_cache *cache,
+                          int32_t *idx, void *k_sel, void *v_sel, int32_t *q_keep, float *scores,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Step 5 alone, on a compacted set supplied by the caller.
+ *   q                [batch][h_q][chunk_len][d]
+ *   k_sel, v_sel     [batch][h_kv][n_sel_max][d]: compacted prior keys, all visible
+ *   n_sel            [batch] int32 (device): rows of k_sel used per sequence, 0..n_sel_max
+ *   k_chunk, v_chunk [batch][h_kv][chunk_len][d]: the chunk's own keys, causal
+ *   out              [batch][h_q][chunk_len][d], element type out_dtype
+ * batch->prior_len_* are not read and may be NULL. */
+kvsel_status kvsel_sparse_attn(const kvsel_heads *heads, const kvsel_batch *batch,
+                               const void *q, const void *k_sel, const void *v_sel,
+                               const int32_t *n_sel, int32_t n_sel_max,
+                               const void *k_chunk, const void *v_chunk,
+                               void *out, int32_t out_dtype,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* One chunk of chunked prefill for every sequence: steps 1-5, then append the
+ * chunk's K/V to the cache at positions [T_b, T_b + chunk_len) (the cache
+ * grows by one chunk; the caller advances T_b).
+ *   q, k_chunk, v_chunk, out  as in kvsel_sparse_attn
+ *   cache   prior rows are read, rows [T_b, T_b + chunk_len) are written;
+ *           capacity (contiguous) or the block table (paged) must cover them
+ *   idx     optional out [batch][h_kv][budget] int32 as in kvsel_select */
+kvsel_status kvsel_prefill_chunk(const kvsel_heads *heads, const kvsel_batch *batch,
+                                 const kvsel_params *params, const void *q,
+                                 const void *k_chunk, const void *v_chunk,
+                                 const kvsel_cache *cache, void *out, int32_t out_dtype,
+                                 int32_t *idx, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/* Text of the last error on the calling thread ("" if none); valid until the
+ * next kvsel_* call on that thread. */
+const char *kvsel_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int32_t kvsel_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSEL_H */

@@ -1,0 +1,246 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Small workloads span several tiles, ragged tails and the
+degenerate cases; the full-size workloads are checked on sampled KV heads /
+sequences in the launch configuration the bench times."""
+import numpy as np
+import pytest
+import torch
+
+import parity
+from chunked_prefill_kv_amd import gen, runner
+from chunked_prefill_kv_amd import kvsel as K
+from oracle import quoka
+
+pytestmark = pytest.mark.gpu
+
+LLAMA = gen.WORKLOADS["llama8b_32k"]
+TINY = gen.WORKLOADS["tiny_f32"]
+SMALL = {
+    "tiny_f32_full": TINY,                                                               # the fp32 workload, whole
+    "f32_d128": TINY.replace(L=600, C=150, d=128, n_q=20, B=200),
+    "bf16_gqa_ragged": LLAMA.replace(L=3000, C=700, H_q=8, H_kv=2, n_q=100, B=900),      # ragged chunk, N_q, B
+    "bf16_mqa": gen.WORKLOADS["mqa_64k"].replace(L=2600, C=512, n_q=40, B=700),          # H_kv = 1, G = 16
+    "bf16_g8_needles": gen.WORKLOADS["gqa_128k"].replace(L=6000, C=1000, H_q=16, H_kv=2, n_q=64, B=1100, needles=8),
+    "bf16_d64": LLAMA.replace(L=2048, C=384, H_q=16, H_kv=2, d=64, n_q=64, B=500),
+    "bf16_nq1": LLAMA.replace(L=1500, C=300, H_q=8, H_kv=2, n_q=1, B=400),               # one kept query per head
+    "bf16_budget1": LLAMA.replace(L=1024, C=256, H_q=4, H_kv=2, n_q=8, B=1),
+    "bf16_keep_all_queries": LLAMA.replace(L=1200, C=100, H_q=4, H_kv=1, n_q=128, B=150),
+    "bf16_dense": LLAMA.replace(L=1000, C=250, H_q=8, H_kv=2, n_q=16, B=1000),           # B >= T always
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    K.load()
+
+
+def _f64(chunks):
+    return [tuple(gen.to_f64(x) for x in c) for c in chunks]
+
+
+def _prior(c64, k):
+    H_kv, d = c64[0][1].shape[0], c64[0][1].shape[2]
+    if k == 0:
+        return np.zeros((H_kv, 0, d)), np.zeros((H_kv, 0, d))
+    return (np.concatenate([c[1] for c in c64[:k]], axis=1), np.concatenate([c[2] for c in c64[:k]], axis=1))
+
+
+def _bits(x: np.ndarray) -> np.ndarray:
+    return x.view(np.uint32) if x.dtype == np.float32 else x
+
+
+def check_chunk(r: runner.PromptRunner, k: int, chunks, c64, heads=None):
+    """select (with debug outputs) then prefill_chunk for chunk k; every rule on KV heads `heads`."""
+    wl = r.wl
+    T, C = r.starts[k], r.lens[k]
+    Qc, Kc, Vc = c64[k]
+    Kp, Vp = _prior(c64, k)
+    dev = r.device
+    nqp = min(wl.n_q, C)
+    idx = torch.full((1, wl.H_kv, wl.B), -7, dtype=torch.int32, device=dev)
+    ks = torch.empty(1, wl.H_kv, wl.B, wl.d, dtype=r.dt, device=dev)
+    vs = torch.empty_like(ks)
+    keep = torch.full((1, wl.H_q, nqp), -7, dtype=torch.int32, device=dev)
+    S = torch.full((1, wl.H_kv, max(T, 1)), float("nan"), dtype=torch.float32, device=dev)
+    K.kvsel_select(r.h, r.batches[k], r.p, r.chunks[k][0], r.cache, idx, ks, vs, keep, S, r.ws)
+    r.run_chunk(k)
+    torch.cuda.synchronize()
+    idx_h = idx[0].cpu().numpy()
+    assert np.array_equal(r.idx[k][0].cpu().numpy(), idx_h), "prefill_chunk and select disagree on idx"
+    G = wl.G
+    heads = range(wl.H_kv) if heads is None else heads
+    qh = [h for g in heads for h in range(g * G, (g + 1) * G)]
+    if T > wl.B:
+        keep_h = keep[0].cpu().numpy()
+        for h in qh:
+            parity.check_keep(Qc[h], wl.n_q, keep_h[h])
+        keep_list = [np.sort(keep_h[h]) for h in range(wl.H_q)]
+        S_h = S[0].cpu().numpy()
+        for g in heads:
+            S_or = quoka.key_scores(Qc[g * G:(g + 1) * G], keep_list[g * G:(g + 1) * G], Kp[g:g + 1])[0]
+            parity.check_close(S_h[g, :T], S_or, parity.S_TOL, f"S chunk {k} head {g}")
+            parity.check_idx(S_or, wl.B, idx_h[g], S_h[g, :T])
+    else:
+        for g in heads:
+            assert np.array_equal(idx_h[g, :T], np.arange(T)) and np.all(idx_h[g, T:] == -1)
+    # gather: bit-exact copies of the cache rows
+    kbits = [_bits(np.concatenate([c[1] for c in chunks[:k]], axis=1)) if k else None]
+    vbits = [_bits(np.concatenate([c[2] for c in chunks[:k]], axis=1)) if k else None]
+    ks_h, vs_h = _bits(runner.to_host_bits(ks[0])), _bits(runner.to_host_bits(vs[0]))
+    n = min(wl.B, T)
+    for g in heads:
+        if n:
+            assert np.array_equal(ks_h[g, :n], kbits[0][g, idx_h[g, :n]]), "gathered K not bit-exact"
+            assert np.array_equal(vs_h[g, :n], vbits[0][g, idx_h[g, :n]]), "gathered V not bit-exact"
+    # attention given the GPU's index set
+    sel_k = [Kp[g, idx_h[g, :n]] for g in range(wl.H_kv)]
+    sel_v = [Vp[g, idx_h[g, :n]] for g in range(wl.H_kv)]
+    Og = r.outs[k][0].double().cpu().numpy()
+    for g in heads:
+        O_or = quoka.attend(Qc[g * G:(g + 1) * G], sel_k[g:g + 1], sel_v[g:g + 1], Kc[g:g + 1], Vc[g:g + 1])
+        parity.check_close(Og[g * G:(g + 1) * G], O_or, parity.o_tol(wl.dtype), f"O chunk {k} head {g}")
+    return idx_h
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_prefill_matches_oracle(name):
+    wl = SMALL[name]
+    print(f"[case] prefill {name} {wl}", flush=True)
+    chunks = [gen.chunk_inputs(wl, k) for k in range(wl.n_chunks)]
+    if name == "bf16_gqa_ragged":                       # a zero key: cosine 0 by convention
+        chunks[0][1][1, 5] = 0
+    c64 = _f64(chunks)
+    r = runner.PromptRunner(wl, out_dtype=torch.float32)
+    r.load(chunks, keep_idx=True)
+    for k in range(wl.n_chunks):
+        check_chunk(r, k, chunks, c64)
+
+
+def test_needles_are_recalled():
+    """Planted keys aligned with one chunk query (cos 0.9) are kept when that chunk is processed."""
+    wl = SMALL["bf16_g8_needles"]
+    chunks = [gen.chunk_inputs(wl, k) for k in range(wl.n_chunks)]
+    r = runner.PromptRunner(wl)
+    r.load(chunks, keep_idx=True)
+    r.run()
+    torch.cuda.synchronize()
+    hit = 0
+    for nd in gen.needles(wl):
+        hit += int(nd.pos in set(r.idx[nd.chunk][0, nd.head // wl.G].cpu().numpy().tolist()))
+    print(f"needle recall {hit}/{len(gen.needles(wl))}")
+    assert hit >= len(gen.needles(wl)) // 2
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sparse_attn_given_oracle_set(dtype):
+    """Rule 2: attention over the oracle's own compacted set, including ragged
+    per-sequence counts and an empty set."""
+    wl = (LLAMA.replace(L=2100, C=700, H_q=8, H_kv=2, n_q=100, B=900) if dtype == "bf16"
+          else TINY.replace(L=512, C=128, n_q=16, B=200))
+    chunks = [gen.chunk_inputs(wl, k) for k in range(wl.n_chunks)]
+    c64 = _f64(chunks)
+    k = wl.n_chunks - 1
+    Qc, Kc, Vc = c64[k]
+    Kp, Vp = _prior(c64, k)
+    sel = quoka.select(Qc, Kp, wl.n_q, wl.B)
+    idx = sel["idx"]
+    nmax = wl.B + 37
+    counts = [len(idx[0]), 0, 13]
+    bsz = len(counts)
+    store = np.uint16 if dtype == "bf16" else np.float32
+    ksel = np.zeros((bsz, wl.H_kv, nmax, wl.d), dtype=store)
+    vsel = np.zeros_like(ksel)
+    kbits = np.concatenate([c[1] for c in chunks[:k]], axis=1)
+    vbits = np.concatenate([c[2] for c in chunks[:k]], axis=1)
+    for b, n in enumerate(counts):
+        for g in range(wl.H_kv):
+            ksel[b, g, :n] = kbits[g, idx[g][:n]]
+            vsel[b, g, :n] = vbits[g, idx[g][:n]]
+    dev = "cuda"
+    tq = runner.to_device(np.stack([chunks[k][0]] * bsz), dev)
+    tkc = runner.to_device(np.stack([chunks[k][1]] * bsz), dev)
+    tvc = runner.to_device(np.stack([chunks[k][2]] * bsz), dev)
+    tks, tvs = runner.to_device(ksel, dev), runner.to_device(vsel, dev)
+    nsel = torch.tensor(counts, dtype=torch.int32, device=dev)
+    h = K.heads(wl.H_q, wl.H_kv, wl.d, K.KVSEL_BF16 if dtype == "bf16" else K.KVSEL_F32)
+    bt = K.batch([0] * bsz, gen.chunk_lengths(wl)[k], None)
+    ws = torch.empty(K.sparse_attn_workspace_size(h, bt, nmax), dtype=torch.uint8, device=dev)
+    out = torch.empty(bsz, wl.H_q, bt.chunk_len, wl.d, dtype=torch.float32, device=dev)
+    K.kvsel_sparse_attn(h, bt, tq, tks, tvs, nsel, nmax, tkc, tvc, out, ws)
+    torch.cuda.synchronize()
+    O = out.double().cpu().numpy()
+    for b, n in enumerate(counts):
+        ref = quoka.attend(Qc, [Kp[g, idx[g][:n]] for g in range(wl.H_kv)],
+                           [Vp[g, idx[g][:n]] for g in range(wl.H_kv)], Kc, Vc)
+        parity.check_close(O[b], ref, parity.o_tol(dtype), f"sparse_attn seq {b} n_sel {n}")
+
+
+@pytest.mark.parametrize("variant", ["gqa", "mqa_g32"])
+def test_decode_paged_matches_oracle(variant):
+    """Ragged batch, chunk of 1, paged cache with a shuffled block table; some
+    sequences are shorter than the budget (no selection)."""
+    base = gen.WORKLOADS["decode_paged"]
+    wl = (base.replace(batch=6, decode_len_lo=300, decode_len_hi=2500, B=512) if variant == "gqa"
+          else base.replace(batch=3, decode_len_lo=700, decode_len_hi=1800, H_q=32, H_kv=1, B=400))
+    print(f"[case] decode {variant}", flush=True)
+    di = gen.decode_inputs(wl)
+    dr = runner.DecodeRunner(wl, di, out_dtype=torch.float32)
+    T_max = int(di.prior_len.max())
+    S = torch.full((wl.batch, wl.H_kv, T_max), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.full((wl.batch, wl.H_kv, wl.B), -7, dtype=torch.int32, device="cuda")
+    K.kvsel_select(dr.h, dr.b, dr.p, dr.q, dr.cache, idx, None, None, None, S, dr.ws)
+    dr.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), dr.idx.cpu().numpy())
+    O = dr.out.double().cpu().numpy()
+    S_h, idx_h = S.cpu().numpy(), dr.idx.cpu().numpy()
+    pool_k = runner.to_host_bits(dr.k_pool)
+    G = wl.G
+    for b in range(wl.batch):
+        T = int(di.prior_len[b])
+        kp, vp = di.logical_kv(b, wl.block_size)
+        Kp, Vp = gen.to_f64(kp), gen.to_f64(vp)
+        Qc = gen.to_f64(di.q[b])
+        if T > wl.B:
+            S_or = quoka.key_scores(Qc, [np.array([0])] * wl.H_q, Kp)
+            for g in range(wl.H_kv):
+                parity.check_close(S_h[b, g, :T], S_or[g], parity.S_TOL, f"S seq {b} head {g}")
+                parity.check_idx(S_or[g], wl.B, idx_h[b, g], S_h[b, g, :T])
+        n = min(T, wl.B)
+        ref = quoka.attend(Qc, [Kp[g, idx_h[b, g, :n]] for g in range(wl.H_kv)],
+                           [Vp[g, idx_h[b, g, :n]] for g in range(wl.H_kv)],
+                           gen.to_f64(di.k_new[b]), gen.to_f64(di.v_new[b]))
+        parity.check_close(O[b], ref, parity.o_tol(wl.dtype), f"O seq {b}")
+        # the new token's K landed in its paged slot
+        blk = di.block_table[b, T // wl.block_size]
+        assert np.array_equal(pool_k[blk, :, T % wl.block_size], di.k_new[b, :, 0])
+
+
+def test_values_all_one_give_one():
+    """Softmax rows sum to one on the GPU too: V == 1 gives O == 1 (bf16 P rounding only)."""
+    wl = LLAMA.replace(L=1536, C=512, H_q=8, H_kv=2, n_q=64, B=600)
+    chunks = [gen.chunk_inputs(wl, k) for k in range(wl.n_chunks)]
+    one = gen.f32_to_bf16_bits(np.ones(1, dtype=np.float32))[0]
+    chunks = [(q, k, np.full_like(v, one)) for q, k, v in chunks]
+    r = runner.PromptRunner(wl, out_dtype=torch.float32)
+    r.load(chunks)
+    r.run()
+    torch.cuda.synchronize()
+    for o in r.outs:
+        assert float((o - 1).abs().max()) < 4e-3
+
+
+def test_bitwise_deterministic():
+    wl = LLAMA.replace(L=2048, C=512, H_q=8, H_kv=2, n_q=64, B=700)
+    r = runner.PromptRunner(wl)
+    r.load(keep_idx=True)
+    r.run()
+    a = [o.clone() for o in r.outs] + [i.clone() for i in r.idx]
+    r.reset()
+    r.run()
+    b = [o.clone() for o in r.outs] + [i.clone() for i in r.idx]
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
