@@ -1,0 +1,169 @@
+#!/usr/bin/env python3
+"""Benchmark: QuoKA chunked prefill (select + attend) on one MI355X.
+
+One step = one whole prompt of the Llama-3-8B-shaped layer (L=32768 tokens in
+16 chunks of 2048, H_q=32, H_kv=8, d=128, N_q=256, B=4096, bf16) pushed
+through kvsel_prefill_chunk: query sub-selection, key scan, top-B,
+compaction, attention and cache append for every chunk.  Inputs are resident
+in HBM before timing starts.  Prints one JSON line:
+
+  value      prefill tokens/s/layer = L / (time of one step)
+  roofline   the attention kernel (the dominant one): algorithmic FLOP per
+             launch / its average launch time, against bf16 dense MFMA peak;
+             launch times come from HIP events recorded on the launch stream
+             (kvsel_trace_*) over a second pass of the same K steps
+  cpu_baseline  the CPU oracle timed on this host on a bounded sample
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s/layer (select+attend) at 32K ctx; % of HBM/MFMA roofline"
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
+
+
+def algorithmic_work(wl, starts, lens):
+    """Per-chunk algorithmic work of the method (see the design notes):
+    attention: 4*d FLOP per (query row, visible key) pair, H_q*(C*B_eff + C(C+1)/2) pairs;
+    scan: 2*d FLOP per (kept query, prior key) pair, H_q*min(N_q,C)*T pairs, only when T > B;
+    scan bytes: the prior keys read once, H_kv*T*d*2."""
+    att_flop, scan_flop, scan_bytes, att_bytes = [], [], [], []
+    for T, C in zip(starts, lens):
+        beff = min(wl.B, T)
+        att_flop.append(4.0 * wl.d * wl.H_q * (C * beff + C * (C + 1) / 2))
+        esz = 2 if wl.dtype == "bf16" else 4
+        att_bytes.append(esz * wl.d * (2 * wl.H_q * C + 2 * wl.H_kv * (beff + C)))
+        if T > wl.B:
+            scan_flop.append(2.0 * wl.d * wl.H_q * min(wl.n_q, C) * T)
+            scan_bytes.append(esz * wl.H_kv * T * wl.d)
+        else:
+            scan_flop.append(0.0)
+            scan_bytes.append(0.0)
+    return att_flop, att_bytes, scan_flop, scan_bytes
+
+
+def cpu_baseline(wl, chunks, sample_every=8):
+    """The oracle, as it stands, on every `sample_every`-th chunk (the last of each group)."""
+    from chunked_prefill_kv_amd import gen
+    from oracle import quoka
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    ks = list(range(sample_every - 1, len(chunks), sample_every))
+    tokens = 0
+    t_total = 0.0
+    for k in ks:
+        Qc, Kc, Vc = (gen.to_f64(x) for x in chunks[k])
+        Kp = np.concatenate([gen.to_f64(c[1]) for c in chunks[:k]], axis=1)
+        Vp = np.concatenate([gen.to_f64(c[2]) for c in chunks[:k]], axis=1)
+        t0 = time.perf_counter()
+        quoka.prefill_chunk(Qc, Kc, Vc, Kp, Vp, wl.n_q, wl.B)
+        t_total += time.perf_counter() - t0
+        tokens += Qc.shape[1]
+    return {"value": tokens / t_total, "unit": "tokens/s/layer", "cores": cores, "kind": "oracle",
+            "sample": f"chunks {ks} of the {len(chunks)}-chunk prompt (all heads, fp64 numpy), "
+                      f"{tokens} tokens in {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b_32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the kernels shard by KV head "
+              f"with no exchange, but multi-GPU runs are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from chunked_prefill_kv_amd import gen, runner
+    from chunked_prefill_kv_amd import kvsel as K
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    K.load()
+    wl = gen.WORKLOADS[args.workload]
+    print(f"[bench] generating {wl.name} inputs", file=sys.stderr, flush=True)
+    chunks = [gen.chunk_inputs(wl, k) for k in range(wl.n_chunks)]
+    r = runner.PromptRunner(wl, out_dtype=torch.bfloat16)
+    r.load(chunks)
+    torch.cuda.synchronize()
+
+    print(f"[bench] warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        r.run()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(args.steps):
+        r.run()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    value = wl.L / (ms_step / 1e3)
+
+    # per-kernel launch times: the same K steps again with every launch bracketed by events
+    K.trace_start()
+    for _ in range(args.steps):
+        r.run()
+    torch.cuda.synchronize()
+    K.trace_stop()
+    tr = K.trace_read()
+    att_flop, att_bytes, scan_flop, scan_bytes = algorithmic_work(wl, r.starts, r.lens)
+    n_att, ms_att = tr["attn"]
+    att_tflops = sum(att_flop) * args.steps / (ms_att * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(att_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(att_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "attn_mfma_kernel<128,bf16 out>",
+                "launches": n_att, "avg_launch_us": round(ms_att * 1e3 / n_att, 2),
+                "algorithmic_flop_per_launch": sum(att_flop) / len(att_flop)}
+    kernels = {k: {"ms_per_step": round(v[1] / args.steps, 4), "launches_per_step": v[0] // args.steps}
+               for k, v in tr.items()}
+    if "scan" in tr:
+        n_sc, ms_sc = tr["scan"]
+        kernels["scan"]["tflops"] = round(sum(scan_flop) * args.steps / (ms_sc * 1e-3) / 1e12, 1)
+        kernels["scan"]["mfma_frac"] = round(kernels["scan"]["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
+        kernels["scan"]["hbm_gbs"] = round(sum(scan_bytes) * args.steps / (ms_sc * 1e-3) / 1e9, 1)
+    kernels["attn"]["hbm_gbs"] = round(sum(att_bytes) * args.steps / (ms_att * 1e-3) / 1e9, 1)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s/layer", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded shared-direction generator, sinks x4)",
+        "config": {"workload": wl.name, "L": wl.L, "C": wl.C, "H_q": wl.H_q, "H_kv": wl.H_kv, "d": wl.d,
+                   "n_q": wl.n_q, "B": wl.B, "chunks": wl.n_chunks, "out": "bf16"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, chunks)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -4,7 +4,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/kvsel.h"
 #include "launch.h"
@@ -37,6 +39,47 @@ kvsel_status hip_check(hipError_t e, const char* what) {
     } while (0)
 
 constexpr int64_t kMaxLen = int64_t(1) << 30;   // positions fit int32 kernel arithmetic
+
+// ----------------------------------------------------------------------------- tracing
+
+const char* const kKernelNames[KVSEL_K_COUNT] = {"qstats", "qtopk", "qpack", "scan", "topb",
+                                                 "gather", "pack", "attn", "append"};
+
+struct Trace {
+    std::mutex mu;
+    uint32_t mask = 0;
+    struct Rec { int id; hipEvent_t a, b; };
+    std::vector<Rec> recs;
+    std::vector<hipEvent_t> pool;
+    hipEvent_t take() {
+        if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+};
+Trace g_trace;
+
+// Launch `fn` (returning hipError_t), bracketed by events when kernel `id` is traced.
+template <typename F>
+hipError_t traced(int id, hipStream_t st, F&& fn) {
+    hipEvent_t a = nullptr, b = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_trace.mu);
+        if (g_trace.mask & (1u << id)) {
+            a = g_trace.take();
+            b = g_trace.take();
+        }
+    }
+    if (a) (void)hipEventRecord(a, st);
+    const hipError_t e = fn();
+    if (a && b) {
+        (void)hipEventRecord(b, st);
+        std::lock_guard<std::mutex> lk(g_trace.mu);
+        g_trace.recs.push_back({id, a, b});
+    }
+    return e;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -177,15 +220,15 @@ kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, 
     float* S = scores ? scores : at<float>(ws, L.scores);
     if (any) {
         int32_t* keep = q_keep ? q_keep : at<int32_t>(ws, L.keep);
-        KVSEL_TRY(launch_qstats(s, q, T, at<float>(ws, L.qcos), at<float>(ws, L.qrn), st), "query statistics");
-        KVSEL_TRY(launch_topk(s.batch * s.h_q, s.h_q, at<float>(ws, L.qcos), s.C, T, s.C, s.budget, s.nqp, keep, s.nqp,
-                              1, st), "query top-k");
-        KVSEL_TRY(launch_pack_qsel(s, q, keep, s.nqp, at<float>(ws, L.qrn), T, at<void>(ws, L.qsel), at<float>(ws, L.rq), st),
+        KVSEL_TRY(traced(KVSEL_K_QSTATS, st, [&] { return launch_qstats(s, q, T, at<float>(ws, L.qcos), at<float>(ws, L.qrn), st); }), "query statistics");
+        KVSEL_TRY(traced(KVSEL_K_QTOPK, st, [&] { return launch_topk(s.batch * s.h_q, s.h_q, at<float>(ws, L.qcos), s.C, T, s.C, s.budget, s.nqp, keep, s.nqp,
+                              1, st); }), "query top-k");
+        KVSEL_TRY(traced(KVSEL_K_QPACK, st, [&] { return launch_pack_qsel(s, q, keep, s.nqp, at<float>(ws, L.qrn), T, at<void>(ws, L.qsel), at<float>(ws, L.rq), st); }),
                   "query packing");
-        KVSEL_TRY(launch_scan(s, at<void>(ws, L.qsel), at<float>(ws, L.rq), cv, T, S, s.t_max, st), "key scan");
+        KVSEL_TRY(traced(KVSEL_K_SCAN, st, [&] { return launch_scan(s, at<void>(ws, L.qsel), at<float>(ws, L.rq), cv, T, S, s.t_max, st); }), "key scan");
     }
-    KVSEL_TRY(launch_topk(s.batch * s.h_kv, s.h_kv, S, s.t_max, T, 0, s.budget, static_cast<int>(s.budget), idx,
-                          s.budget, 0, st), "key top-B");
+    KVSEL_TRY(traced(KVSEL_K_TOPB, st, [&] { return launch_topk(s.batch * s.h_kv, s.h_kv, S, s.t_max, T, 0, s.budget, static_cast<int>(s.budget), idx,
+                          s.budget, 0, st); }), "key top-B");
     return KVSEL_OK;
 }
 
@@ -194,6 +237,41 @@ kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, 
 extern "C" {
 
 const char* kvsel_last_error(void) { return g_err.c_str(); }
+
+kvsel_status kvsel_trace_start(uint32_t kernel_mask) {
+    g_err.clear();
+    std::lock_guard<std::mutex> lk(g_trace.mu);
+    g_trace.mask = kernel_mask;
+    return KVSEL_OK;
+}
+
+kvsel_status kvsel_trace_stop(void) {
+    g_err.clear();
+    std::lock_guard<std::mutex> lk(g_trace.mu);
+    g_trace.mask = 0;
+    return KVSEL_OK;
+}
+
+kvsel_status kvsel_trace_read(int32_t* launches, float* total_ms, int32_t n) {
+    g_err.clear();
+    if (!launches || !total_ms || n < 0) return fail(KVSEL_ERR_INVALID_ARG, "launches/total_ms is NULL or n < 0");
+    for (int i = 0; i < n; ++i) { launches[i] = 0; total_ms[i] = 0.0f; }
+    std::lock_guard<std::mutex> lk(g_trace.mu);
+    kvsel_status st = KVSEL_OK;
+    for (auto& r : g_trace.recs) {
+        float ms = 0.0f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess && st == KVSEL_OK) st = hip_check(e, "trace event");
+        if (r.id < n) { launches[r.id] += 1; total_ms[r.id] += ms; }
+        g_trace.pool.push_back(r.a);
+        g_trace.pool.push_back(r.b);
+    }
+    g_trace.recs.clear();
+    return st;
+}
+
+const char* kvsel_kernel_name(int32_t id) { return (id >= 0 && id < KVSEL_K_COUNT) ? kKernelNames[id] : ""; }
 
 int32_t kvsel_version(void) { return 100; }
 
@@ -242,7 +320,7 @@ kvsel_status kvsel_select(const kvsel_heads* heads, const kvsel_batch* batch, co
     const CacheView cv = make_view(cache, heads);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if ((st = run_select(s, batch, q, cv, workspace, L, idx, q_keep, scores, hs))) return st;
-    if (k_sel) KVSEL_TRY(launch_gather(s, cv, batch->prior_len_dev, idx, s.budget, k_sel, v_sel, hs), "gather");
+    if (k_sel) KVSEL_TRY(traced(KVSEL_K_GATHER, hs, [&] { return launch_gather(s, cv, batch->prior_len_dev, idx, s.budget, k_sel, v_sel, hs); }), "gather");
     return KVSEL_OK;
 }
 
@@ -276,8 +354,8 @@ kvsel_status kvsel_sparse_attn(const kvsel_heads* heads, const kvsel_batch* batc
     src.n_sel_max = n_sel_max;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const float scale = heads->scale > 0.0f ? heads->scale : 1.0f / std::sqrt(static_cast<float>(heads->d));
-    KVSEL_TRY(launch_pack(s, src, k_chunk, v_chunk, nk_pad, kall, vall, nsel_ws, hs), "pack");
-    KVSEL_TRY(launch_attn(s, q, kall, vall, nsel_ws, nk_pad, scale, out, out_dtype == KVSEL_F32, hs), "attention");
+    KVSEL_TRY(traced(KVSEL_K_PACK, hs, [&] { return launch_pack(s, src, k_chunk, v_chunk, nk_pad, kall, vall, nsel_ws, hs); }), "pack");
+    KVSEL_TRY(traced(KVSEL_K_ATTN, hs, [&] { return launch_attn(s, q, kall, vall, nsel_ws, nk_pad, scale, out, out_dtype == KVSEL_F32, hs); }), "attention");
     return KVSEL_OK;
 }
 
@@ -310,11 +388,11 @@ kvsel_status kvsel_prefill_chunk(const kvsel_heads* heads, const kvsel_batch* ba
     src.idx_stride = s.budget;
     int32_t* nsel = at<int32_t>(workspace, L.nsel);
     const float scale = heads->scale > 0.0f ? heads->scale : 1.0f / std::sqrt(static_cast<float>(heads->d));
-    KVSEL_TRY(launch_pack(s, src, k_chunk, v_chunk, L.nk_pad, at<void>(workspace, L.kall), at<void>(workspace, L.vall),
-                          nsel, hs), "pack");
-    KVSEL_TRY(launch_attn(s, q, at<void>(workspace, L.kall), at<void>(workspace, L.vall), nsel, L.nk_pad, scale, out,
-                          out_dtype == KVSEL_F32, hs), "attention");
-    KVSEL_TRY(launch_append(s, cv, batch->prior_len_dev, k_chunk, v_chunk, hs), "append");
+    KVSEL_TRY(traced(KVSEL_K_PACK, hs, [&] { return launch_pack(s, src, k_chunk, v_chunk, L.nk_pad, at<void>(workspace, L.kall), at<void>(workspace, L.vall),
+                          nsel, hs); }), "pack");
+    KVSEL_TRY(traced(KVSEL_K_ATTN, hs, [&] { return launch_attn(s, q, at<void>(workspace, L.kall), at<void>(workspace, L.vall), nsel, L.nk_pad, scale, out,
+                          out_dtype == KVSEL_F32, hs); }), "attention");
+    KVSEL_TRY(traced(KVSEL_K_APPEND, hs, [&] { return launch_append(s, cv, batch->prior_len_dev, k_chunk, v_chunk, hs); }), "append");
     return KVSEL_OK;
 }
 

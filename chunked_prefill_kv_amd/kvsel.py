@@ -22,7 +22,9 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: 
 
 # the exported symbols of include/kvsel.h
 EXPORTS = ("kvsel_workspace_size", "kvsel_sparse_attn_workspace_size", "kvsel_select", "kvsel_sparse_attn",
-           "kvsel_prefill_chunk", "kvsel_last_error", "kvsel_version")
+           "kvsel_prefill_chunk", "kvsel_last_error", "kvsel_version", "kvsel_trace_start", "kvsel_trace_stop",
+           "kvsel_trace_read", "kvsel_kernel_name")
+KERNELS = ("qstats", "qtopk", "qpack", "scan", "topb", "gather", "pack", "attn", "append")
 
 
 class Heads(ctypes.Structure):
@@ -76,6 +78,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvsel_last_error.restype = ctypes.c_char_p
     lib.kvsel_version.argtypes = []
     lib.kvsel_version.restype = ctypes.c_int32
+    lib.kvsel_trace_start.argtypes = [ctypes.c_uint32]
+    lib.kvsel_trace_stop.argtypes = []
+    lib.kvsel_trace_read.argtypes = [P(ctypes.c_int32), P(ctypes.c_float), i32]
+    for name in ("kvsel_trace_start", "kvsel_trace_stop", "kvsel_trace_read"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.kvsel_kernel_name.argtypes = [i32]
+    lib.kvsel_kernel_name.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -155,6 +164,27 @@ def kvsel_prefill_chunk(h: Heads, b: Batch, p: Params, q: torch.Tensor, k_chunk:
                                       k_chunk.data_ptr(), v_chunk.data_ptr(), ctypes.byref(c), out.data_ptr(),
                                       dtype_code(out), _ptr(idx), ws.data_ptr(), ws.numel() * ws.element_size(),
                                       _stream()))
+
+
+def trace_start(kernels=KERNELS) -> None:
+    """Bracket every later launch of the named kernels with HIP events on its stream."""
+    mask = 0
+    for k in kernels:
+        mask |= 1 << KERNELS.index(k)
+    _check(load().kvsel_trace_start(mask))
+
+
+def trace_stop() -> None:
+    _check(load().kvsel_trace_stop())
+
+
+def trace_read() -> dict:
+    """{kernel: (launches, total_ms)} for the traced launches since the last read."""
+    n = len(KERNELS)
+    launches = (ctypes.c_int32 * n)()
+    ms = (ctypes.c_float * n)()
+    _check(load().kvsel_trace_read(launches, ms, n))
+    return {KERNELS[i]: (launches[i], ms[i]) for i in range(n) if launches[i]}
 
 
 def last_error() -> str:

@@ -150,6 +150,34 @@ kvsel_status kvsel_prefill_chunk(const kvsel_heads *heads, const kvsel_batch *ba
                                  int32_t *idx, void *workspace, size_t workspace_bytes,
                                  void *stream);
 
+/* Per-kernel timing (a tracing aid for benchmarks).  After
+ * kvsel_trace_start(mask), every launch of a kernel whose bit (1 << id) is
+ * set in `mask` is bracketed by two hipEvents recorded on its launch stream;
+ * kvsel_trace_stop() ends recording.  kvsel_trace_read() waits for the
+ * recorded events and writes, for every kernel id < n, the number of launches
+ * and their summed duration in milliseconds into the [host] arrays
+ * `launches` and `total_ms`, then clears the record.  The library creates the
+ * events itself (no device memory) and reuses them.  Tracing state is global
+ * to the process and guarded by a mutex. */
+typedef enum {
+    KVSEL_K_QSTATS = 0,   /* step 1: query cosines to the mean query, 1/|q| */
+    KVSEL_K_QTOPK = 1,    /* step 1: the kept queries (exact top-k) */
+    KVSEL_K_QPACK = 2,    /* step 1: kept query rows packed per KV head */
+    KVSEL_K_SCAN = 3,     /* step 2: cosine key scores over the prior cache */
+    KVSEL_K_TOPB = 4,     /* step 3: per-KV-head top-B */
+    KVSEL_K_GATHER = 5,   /* step 4 (kvsel_select): k_sel/v_sel rows */
+    KVSEL_K_PACK = 6,     /* step 4: compacted keys + chunk keys for attention */
+    KVSEL_K_ATTN = 7,     /* step 5: attention */
+    KVSEL_K_APPEND = 8,   /* cache append */
+    KVSEL_K_COUNT = 9
+} kvsel_kernel;
+
+kvsel_status kvsel_trace_start(uint32_t kernel_mask);
+kvsel_status kvsel_trace_stop(void);
+kvsel_status kvsel_trace_read(int32_t *launches, float *total_ms, int32_t n);
+/* Short name of kernel id (e.g. "attn"); "" for an unknown id. */
+const char *kvsel_kernel_name(int32_t id);
+
 /* Text of the last error on the calling thread ("" if none); valid until the
  * next kvsel_* call on that thread. */
 const char *kvsel_last_error(void);
