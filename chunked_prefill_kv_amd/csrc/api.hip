@@ -175,7 +175,7 @@ SelShape make_shape(const kvsel_heads* h, const kvsel_batch* b, const kvsel_para
 // ----------------------------------------------------------------------------- workspace layout
 
 struct Layout {
-    size_t qcos, qrn, keep, qsel, rq, scores, idx, nsel, kall, vall, total;
+    size_t qpart, qcos, qrn, keep, qsel, rq, scores, idx, nsel, kall, vall, total;
     int nk_pad;
 };
 
@@ -184,6 +184,7 @@ Layout layout(const SelShape& s, bool with_attn) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     const size_t bh = size_t(s.batch) * s.h_q, bg = size_t(s.batch) * s.h_kv;
+    L.qpart = take(size_t(qstats_part_elems(s)) * 8);
     L.qcos = take(bh * s.C * 4);
     L.qrn = take(bh * s.C * 4);
     L.keep = take(bh * s.nqp * 4);
@@ -220,15 +221,15 @@ kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, 
     float* S = scores ? scores : at<float>(ws, L.scores);
     if (any) {
         int32_t* keep = q_keep ? q_keep : at<int32_t>(ws, L.keep);
-        KVSEL_TRY(traced(KVSEL_K_QSTATS, st, [&] { return launch_qstats(s, q, T, at<float>(ws, L.qcos), at<float>(ws, L.qrn), st); }), "query statistics");
+        KVSEL_TRY(traced(KVSEL_K_QSTATS, st, [&] { return launch_qstats(s, q, T, at<double>(ws, L.qpart), at<float>(ws, L.qcos), at<float>(ws, L.qrn), st); }), "query statistics");
         KVSEL_TRY(traced(KVSEL_K_QTOPK, st, [&] { return launch_topk(s.batch * s.h_q, s.h_q, at<float>(ws, L.qcos), s.C, T, s.C, s.budget, s.nqp, keep, s.nqp,
-                              1, st); }), "query top-k");
+                              1, s.C, st); }), "query top-k");
         KVSEL_TRY(traced(KVSEL_K_QPACK, st, [&] { return launch_pack_qsel(s, q, keep, s.nqp, at<float>(ws, L.qrn), T, at<void>(ws, L.qsel), at<float>(ws, L.rq), st); }),
                   "query packing");
         KVSEL_TRY(traced(KVSEL_K_SCAN, st, [&] { return launch_scan(s, at<void>(ws, L.qsel), at<float>(ws, L.rq), cv, T, S, s.t_max, st); }), "key scan");
     }
     KVSEL_TRY(traced(KVSEL_K_TOPB, st, [&] { return launch_topk(s.batch * s.h_kv, s.h_kv, S, s.t_max, T, 0, s.budget, static_cast<int>(s.budget), idx,
-                          s.budget, 0, st); }), "key top-B");
+                          s.budget, 0, s.t_max, st); }), "key top-B");
     return KVSEL_OK;
 }
 

@@ -24,10 +24,6 @@ __device__ __forceinline__ int sigma(int m) {
     return 16 * (a >> 1) + 8 * hb + 4 * (a & 1) + c;
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
-}
-
 }  // namespace
 
 // ----------------------------------------------------------------------------- bf16 MFMA kernel

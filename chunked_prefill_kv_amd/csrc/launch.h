@@ -20,17 +20,21 @@ struct SelShape {
 
 // Step 1: per (b, h) cosine of each chunk query to the mean query (selection
 // key) and 1/|q| of each query.  Sequences with T_b <= budget are skipped.
-hipError_t launch_qstats(const SelShape& s, const void* q, const int64_t* prior_len,
+// part: fp64 scratch of qstats_part_elems(s) elements.
+hipError_t launch_qstats(const SelShape& s, const void* q, const int64_t* prior_len, double* part,
                          float* qcos, float* qrn, hipStream_t st);
+inline int64_t qstats_part_elems(const SelShape& s) {
+    return int64_t(s.batch) * s.h_q * ((s.C + 255) / 256) * s.d;
+}
 
 // Exact top-k with lower-index tie-break, indices ascending, -1 padded to k.
 //   mode 0: the k largest of scores[p][0..n_p)      (n_p = prior_len[p / heads_per_seq])
 //   mode 1: the k smallest of scores[p][0..n_fixed) (query keep); problems
 //           whose sequence has T_b <= budget are skipped
-// When n_p <= k every index [0, n_p) is taken.
+// When n_p <= k every index [0, n_p) is taken.  max_n bounds every n_p.
 hipError_t launch_topk(int problems, int heads_per_seq, const float* scores, int64_t score_stride,
                        const int64_t* prior_len, int n_fixed, int64_t budget, int k,
-                       int32_t* out, int64_t out_stride, int mode, hipStream_t st);
+                       int32_t* out, int64_t out_stride, int mode, int64_t max_n, hipStream_t st);
 
 // Gather the kept query rows of every head into Q_sel[b][g][hh*nq_pad + r][d]
 // (raw rows) and rq = 1/|q|; rows r >= nqp repeat row 0 of that head.

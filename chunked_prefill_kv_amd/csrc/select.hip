@@ -33,59 +33,101 @@ template <> struct Vec8<float> {      // 8 fp32 = two 16-byte loads
 };
 
 // ----------------------------------------------------------------------------- step 1 statistics
+//
+// Two passes over the chunk's queries, both spread over (head, 256-row block)
+// workgroups with coalesced 16-byte loads.  Sums, dot products and norms are
+// accumulated in fp64 (the inputs are exact in fp32), so the selection key
+// carries only its final fp32 rounding.
 
-// One workgroup per (sequence, query head).  The mean query and every dot
-// product / norm are accumulated in fp64 (the inputs are exact in fp32), so
-// the selection key carries only the final fp32 rounding.
+constexpr int kQRows = 256;   // query rows per workgroup
+
+// pass 1: per (head, row block) column sums of the query rows -> part[bh][blk][D] (fp64)
 template <typename T, int D>
-__global__ __launch_bounds__(256) void qstats_kernel(const T* __restrict__ q, int h_q, int C,
-                                                     const int64_t* __restrict__ prior_len, int64_t budget,
-                                                     float* __restrict__ qcos, float* __restrict__ qrn) {
-    const int bh = blockIdx.x;
-    const int b = bh / h_q;
-    if (prior_len[b] <= budget) return;
+__global__ __launch_bounds__(256) void qsum_kernel(const T* __restrict__ q, int h_q, int C, int nblk,
+                                                   const int64_t* __restrict__ prior_len, int64_t budget,
+                                                   double* __restrict__ part) {
+    constexpr int G8 = D / 8;                 // 8-column groups per row
+    constexpr int RPP = 256 / G8;             // rows per pass
+    const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
+    if (prior_len[bh / h_q] <= budget) return;
     const T* qh = q + static_cast<int64_t>(bh) * C * D;
-    constexpr int kSub = 256 / D;
-    __shared__ double part[kSub][D];
-    __shared__ double mean[D];
-    __shared__ double mnorm;
-    const int c = threadIdx.x % D, sub = threadIdx.x / D;
-    double acc = 0.0;
-    for (int r = sub; r < C; r += kSub) acc += static_cast<double>(Elem<T>::load(qh, static_cast<int64_t>(r) * D + c));
-    part[sub][c] = acc;
+    const int c8 = threadIdx.x % G8, sub = threadIdx.x / G8;
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int r1 = min(C, (blk + 1) * kQRows);
+    for (int r = blk * kQRows + sub; r < r1; r += RPP) {
+        float x[8];
+        Vec8<T>::load(qh + static_cast<int64_t>(r) * D + c8 * 8, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += static_cast<double>(x[i]);
+    }
+    __shared__ double red[RPP][D];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[sub][c8 * 8 + i] = acc[i];
     __syncthreads();
     if (threadIdx.x < D) {
         double s = 0.0;
-#pragma unroll
-        for (int k = 0; k < kSub; ++k) s += part[k][threadIdx.x];
+        for (int k = 0; k < RPP; ++k) s += red[k][threadIdx.x];
+        part[(static_cast<int64_t>(bh) * nblk + blk) * D + threadIdx.x] = s;
+    }
+}
+
+// pass 2: mean query from the partial sums, then cos(q_i, mean) and 1/|q_i| per row
+template <typename T, int D>
+__global__ __launch_bounds__(256) void qcos_kernel(const T* __restrict__ q, int h_q, int C, int nblk,
+                                                   const int64_t* __restrict__ prior_len, int64_t budget,
+                                                   const double* __restrict__ part, float* __restrict__ qcos,
+                                                   float* __restrict__ qrn) {
+    constexpr int G8 = D / 8;
+    constexpr int RPP = 256 / G8;
+    const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
+    if (prior_len[bh / h_q] <= budget) return;
+    __shared__ double mean[D];
+    __shared__ double mnorm;
+    if (threadIdx.x < D) {
+        double s = 0.0;
+        for (int k = 0; k < nblk; ++k) s += part[(static_cast<int64_t>(bh) * nblk + k) * D + threadIdx.x];
         mean[threadIdx.x] = s / C;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (threadIdx.x < kWave) {
         double s = 0.0;
-        for (int e = 0; e < D; ++e) s += mean[e] * mean[e];
-        mnorm = sqrt(s);
+        for (int e = threadIdx.x; e < D; e += kWave) s += mean[e] * mean[e];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
+        if (threadIdx.x == 0) mnorm = sqrt(s);
     }
     __syncthreads();
+    const int c8 = threadIdx.x % G8, sub = threadIdx.x / G8;
+    double m[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m[i] = mean[c8 * 8 + i];
     const double mn = mnorm;
-    for (int r = threadIdx.x; r < C; r += 256) {
-        const T* row = qh + static_cast<int64_t>(r) * D;
+    const T* qh = q + static_cast<int64_t>(bh) * C * D;
+    const int r1 = min(C, (blk + 1) * kQRows);
+    for (int r0 = blk * kQRows; r0 < r1; r0 += RPP) {      // uniform trip count: shuffles stay converged
+        const int r = r0 + sub;
         double dot = 0.0, n2 = 0.0;
-#pragma unroll 2
-        for (int e0 = 0; e0 < D; e0 += 8) {
+        if (r < r1) {
             float x[8];
-            Vec8<T>::load(row + e0, x);
+            Vec8<T>::load(qh + static_cast<int64_t>(r) * D + c8 * 8, x);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const double xd = x[i];
-                dot += xd * mean[e0 + i];
+                dot += xd * m[i];
                 n2 += xd * xd;
             }
         }
-        const double nq = sqrt(n2);
-        const double den = nq * mn;
-        qcos[static_cast<int64_t>(bh) * C + r] = den > 0.0 ? static_cast<float>(dot / den) : 0.0f;
-        qrn[static_cast<int64_t>(bh) * C + r] = nq > 0.0 ? static_cast<float>(1.0 / nq) : 0.0f;
+#pragma unroll
+        for (int o = G8 / 2; o >= 1; o >>= 1) {               // reduce over the row's lanes
+            dot += __shfl_xor(dot, o, kWave);
+            n2 += __shfl_xor(n2, o, kWave);
+        }
+        if (c8 == 0 && r < r1) {
+            const double nq = sqrt(n2);
+            const double den = nq * mn;
+            qcos[static_cast<int64_t>(bh) * C + r] = den > 0.0 ? static_cast<float>(dot / den) : 0.0f;
+            qrn[static_cast<int64_t>(bh) * C + r] = nq > 0.0 ? static_cast<float>(1.0 / nq) : 0.0f;
+        }
     }
 }
 
@@ -118,6 +160,9 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
     return off + incl - v;
 }
 
+constexpr int kLdsKeys = 30720;   // problems up to this size keep their keys in LDS (120 KB)
+
+template <bool kLds>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores, int64_t score_stride,
                                                             int heads_per_seq, const int64_t* __restrict__ prior_len,
                                                             int n_fixed, int64_t budget, int k,
@@ -141,7 +186,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
         return;
     }
     const uint32_t flip = mode ? 0xFFFFFFFFu : 0u;   // mode 1 keeps the smallest
-    auto key = [&](int j) -> uint32_t { return order_key(x[j]) ^ flip; };
+    __shared__ uint32_t kc[kLds ? kLdsKeys : 1];      // the problem's order keys when they fit
+    auto gkey = [&](int j) -> uint32_t { return order_key(x[j]) ^ flip; };
+    auto key = [&](int j) -> uint32_t { return kLds ? kc[j] : gkey(j); };
 
     __shared__ uint32_t hist[kHistBins];
     __shared__ uint32_t wsum[kTopkWaves];
@@ -149,9 +196,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     __shared__ uint32_t s_digit, s_rem;
 
     // bits shared by every key need no histogram pass
-    const uint32_t first = key(0);
+    const uint32_t first = gkey(0);
     uint32_t diff = 0;
-    for (int j = tid; j < n; j += kTopkThreads) diff |= key(j) ^ first;
+    for (int j = tid; j < n; j += kTopkThreads) {
+        const uint32_t u = gkey(j);
+        if (kLds) kc[j] = u;
+        diff |= u ^ first;
+    }
 #pragma unroll
     for (int o2 = 32; o2 >= 1; o2 >>= 1) diff |= __shfl_xor(diff, o2, kWave);
     if (lane == 0) wsum[wave] = diff;
@@ -261,24 +312,37 @@ __global__ __launch_bounds__(256) void pack_qsel_kernel(const T* __restrict__ q,
 
 // ----------------------------------------------------------------------------- launchers
 
-hipError_t launch_qstats(const SelShape& s, const void* q, const int64_t* prior_len, float* qcos, float* qrn,
-                         hipStream_t st) {
-    dim3 grid(s.batch * s.h_q), block(256);
+hipError_t launch_qstats(const SelShape& s, const void* q, const int64_t* prior_len, double* part, float* qcos,
+                         float* qrn, hipStream_t st) {
+    const int nblk = (s.C + kQRows - 1) / kQRows;
+    dim3 grid(s.batch * s.h_q * nblk), block(256);
+#define KVSEL_QSTATS(T, D)                                                                                         \
+    do {                                                                                                           \
+        hipLaunchKernelGGL((qsum_kernel<T, D>), grid, block, 0, st, (const T*)q, s.h_q, s.C, nblk, prior_len,      \
+                           s.budget, part);                                                                        \
+        hipLaunchKernelGGL((qcos_kernel<T, D>), grid, block, 0, st, (const T*)q, s.h_q, s.C, nblk, prior_len,      \
+                           s.budget, part, qcos, qrn);                                                             \
+    } while (0)
     if (s.esz == 2) {
-        if (s.d == 128) hipLaunchKernelGGL((qstats_kernel<uint16_t, 128>), grid, block, 0, st, (const uint16_t*)q, s.h_q, s.C, prior_len, s.budget, qcos, qrn);
-        else hipLaunchKernelGGL((qstats_kernel<uint16_t, 64>), grid, block, 0, st, (const uint16_t*)q, s.h_q, s.C, prior_len, s.budget, qcos, qrn);
+        if (s.d == 128) KVSEL_QSTATS(uint16_t, 128);
+        else KVSEL_QSTATS(uint16_t, 64);
     } else {
-        if (s.d == 128) hipLaunchKernelGGL((qstats_kernel<float, 128>), grid, block, 0, st, (const float*)q, s.h_q, s.C, prior_len, s.budget, qcos, qrn);
-        else hipLaunchKernelGGL((qstats_kernel<float, 64>), grid, block, 0, st, (const float*)q, s.h_q, s.C, prior_len, s.budget, qcos, qrn);
+        if (s.d == 128) KVSEL_QSTATS(float, 128);
+        else KVSEL_QSTATS(float, 64);
     }
+#undef KVSEL_QSTATS
     return hipGetLastError();
 }
 
 hipError_t launch_topk(int problems, int heads_per_seq, const float* scores, int64_t score_stride,
                        const int64_t* prior_len, int n_fixed, int64_t budget, int k, int32_t* out,
-                       int64_t out_stride, int mode, hipStream_t st) {
-    hipLaunchKernelGGL(topk_kernel, dim3(problems), dim3(kTopkThreads), 0, st, scores, score_stride, heads_per_seq,
-                       prior_len, n_fixed, budget, k, out, out_stride, mode);
+                       int64_t out_stride, int mode, int64_t max_n, hipStream_t st) {
+    if (max_n <= kLdsKeys)
+        hipLaunchKernelGGL(topk_kernel<true>, dim3(problems), dim3(kTopkThreads), 0, st, scores, score_stride,
+                           heads_per_seq, prior_len, n_fixed, budget, k, out, out_stride, mode);
+    else
+        hipLaunchKernelGGL(topk_kernel<false>, dim3(problems), dim3(kTopkThreads), 0, st, scores, score_stride,
+                           heads_per_seq, prior_len, n_fixed, budget, k, out, out_stride, mode);
     return hipGetLastError();
 }
 
