@@ -86,6 +86,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lib", default=None, help="path of an alternative libkvsel.so build")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the kernels shard by KV head "
@@ -97,7 +98,7 @@ def main():
     from chunked_prefill_kv_amd import kvsel as K
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    K.load()
+    K.load(args.lib) if args.lib else K.load()
     wl = gen.WORKLOADS[args.workload]
     print(f"[bench] generating {wl.name} inputs", file=sys.stderr, flush=True)
     chunks = [gen.chunk_inputs(wl, k) for k in range(wl.n_chunks)]

@@ -29,9 +29,9 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, src.replace(".hip", ".o"))
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
@@ -42,19 +42,21 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = True, lib: str = LIB, build_dir: str = BUILD, extra=()) -> str:
+    """Compile every source and link `lib`.  `extra` adds hipcc flags (e.g. -D options
+    selecting a tile variant); the default build uses none."""
+    os.makedirs(build_dir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, build_dir, extra), SOURCES))
+    tmp = lib + ".tmp"
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    shutil.move(tmp, LIB)
+    shutil.move(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":

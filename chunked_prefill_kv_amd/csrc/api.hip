@@ -387,13 +387,14 @@ kvsel_status kvsel_prefill_chunk(const kvsel_heads* heads, const kvsel_batch* ba
     src.budget = s.budget;
     src.idx = idx_buf;
     src.idx_stride = s.budget;
+    src.append = true;
     int32_t* nsel = at<int32_t>(workspace, L.nsel);
     const float scale = heads->scale > 0.0f ? heads->scale : 1.0f / std::sqrt(static_cast<float>(heads->d));
     KVSEL_TRY(traced(KVSEL_K_PACK, hs, [&] { return launch_pack(s, src, k_chunk, v_chunk, L.nk_pad, at<void>(workspace, L.kall), at<void>(workspace, L.vall),
                           nsel, hs); }), "pack");
     KVSEL_TRY(traced(KVSEL_K_ATTN, hs, [&] { return launch_attn(s, q, at<void>(workspace, L.kall), at<void>(workspace, L.vall), nsel, L.nk_pad, scale, out,
                           out_dtype == KVSEL_F32, hs); }), "attention");
-    KVSEL_TRY(traced(KVSEL_K_APPEND, hs, [&] { return launch_append(s, cv, batch->prior_len_dev, k_chunk, v_chunk, hs); }), "append");
+    // the cache append happens inside the pack kernel (it reads the chunk's rows anyway)
     return KVSEL_OK;
 }
 

@@ -9,6 +9,8 @@
 // (token, head-in-group) rows of all G heads of a KV head and stages each key
 // tile in LDS once for all of them.  Multi-query attention page, "Teknisk
 // innsikt": each query head uses its own query against the shared K/V.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace kvsel {
@@ -19,6 +21,16 @@ namespace {
 // 32x32x16 result tile S^T (keys x queries) leaves, in every lane, 8
 // consecutive keys per 16-key block in 8 consecutive registers - exactly the
 // B operand of the P.V MFMA, so P never leaves registers.
+// max over lanes l and l ^ 32 (v_permlane32_swap exchanges the two half-waves)
+__device__ __forceinline__ float half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ int sigma(int m) {
     const int a = m >> 3, hb = (m >> 2) & 1, c = m & 3;
     return 16 * (a >> 1) + 8 * hb + 4 * (a & 1) + c;
@@ -33,8 +45,16 @@ __device__ __forceinline__ int sigma(int m) {
 // Per 64-key tile: S^T = K . Q^T (2 x KS MFMAs), online softmax on the lane's
 // query column, O^T += V^T . P^T (DB x 4 MFMAs).  K tiles are row-major
 // [key][d] and V tiles are [d][key] (written transposed by the pack kernel).
-template <int D, bool OUT_F32>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const uint16_t* __restrict__ q,
+#ifndef KVSEL_ATTN_KT
+#define KVSEL_ATTN_KT 64
+#endif
+#ifndef KVSEL_ATTN_PRIO
+#define KVSEL_ATTN_PRIO 1
+#endif
+#define KVSEL_SETPRIO(p) do { if (KVSEL_ATTN_PRIO) __builtin_amdgcn_s_setprio(p); } while (0)
+
+template <int D, bool OUT_F32, int KT>
+__global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void attn_mfma_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ kall,
                                                            const uint16_t* __restrict__ vall,
                                                            const int32_t* __restrict__ nsel, int nk_pad, int C, int G,
@@ -42,7 +62,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const uint16_t* __res
                                                            void* __restrict__ out) {
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
-    constexpr int KT = 64;
+    constexpr int NKB = KT / 32;            // 32-key MFMA blocks per tile
     constexpr int LDK = D + 8;
     constexpr int LDV = KT + 8;
     constexpr int PK = KT * D / 8 / 256;    // 16-byte K pieces per thread per tile
@@ -82,33 +102,41 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const uint16_t* __res
 
     const uint16_t* kb = kall + static_cast<int64_t>(bg) * nk_pad * D;
     const uint16_t* vb = vall + static_cast<int64_t>(bg) * D * nk_pad;
-    u32x4 pk[PK], pv[PV];
-    auto fetch = [&](int t) {
+    // Next-tile staging in two halves: K(t+1) is fetched at the start of tile t
+    // and written to LDS after t's S MFMAs, V(t+1) is fetched then and written
+    // at the end of t.  Buffer (t+1)&1 was last read in tile t-1, which every
+    // wave finished before the barrier that closed it, so both writes are safe.
+    u32x4 pst[PK > PV ? PK : PV];
+    auto fetch_k = [&](int t) {
 #pragma unroll
         for (int i = 0; i < PK; ++i) {
             const int p = tid + 256 * i;
             const int r = p / (D / 8), c = p % (D / 8);
-            pk[i] = *reinterpret_cast<const u32x4*>(kb + static_cast<int64_t>(t * KT + r) * D + c * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < PV; ++i) {
-            const int p = tid + 256 * i;
-            const int d = p / (KT / 8), j = p % (KT / 8);
-            pv[i] = *reinterpret_cast<const u32x4*>(vb + static_cast<int64_t>(d) * nk_pad + t * KT + j * 8);
+            pst[i] = *reinterpret_cast<const u32x4*>(kb + static_cast<int64_t>(t * KT + r) * D + c * 8);
         }
     };
-    auto stash = [&](int buf) {
+    auto stash_k = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < PK; ++i) {
             const int p = tid + 256 * i;
             const int r = p / (D / 8), c = p % (D / 8);
-            *reinterpret_cast<u32x4*>(&k_lds[buf][r * LDK + c * 8]) = pk[i];
+            *reinterpret_cast<u32x4*>(&k_lds[buf][r * LDK + c * 8]) = pst[i];
         }
+    };
+    auto fetch_v = [&](int t) {
 #pragma unroll
         for (int i = 0; i < PV; ++i) {
             const int p = tid + 256 * i;
             const int d = p / (KT / 8), j = p % (KT / 8);
-            *reinterpret_cast<u32x4*>(&v_lds[buf][d * LDV + j * 8]) = pv[i];
+            pst[i] = *reinterpret_cast<const u32x4*>(vb + static_cast<int64_t>(d) * nk_pad + t * KT + j * 8);
+        }
+    };
+    auto stash_v = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < PV; ++i) {
+            const int p = tid + 256 * i;
+            const int d = p / (KT / 8), j = p % (KT / 8);
+            *reinterpret_cast<u32x4*>(&v_lds[buf][d * LDV + j * 8]) = pst[i];
         }
     };
 
@@ -119,81 +147,112 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const uint16_t* __res
     const int krow = sigma(col);
     const int lim = n_s + tok;                  // last visible slot of this lane's query
 
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < ntiles) fetch(t + 1);
-        const int s0 = t * KT;
-        if (wave_active && s0 <= n_s + w_tmax) {
-            f32x16 sacc[2];
+    // One KT-key tile: S^T, online softmax, O^T += V^T P^T.  MASK applies the
+    // causal limit (only tiles that reach past the wave's first token need it).
+    // The running max is only moved when it grows by more than 2^8 (log2
+    // units): p = exp2(s*cl2 - m*cl2) then stays <= 256 and O, l share the same
+    // reference, so the result is unchanged while most tiles skip the rescale.
+    auto tile = [&](const int buf, const int s0, auto mask_tag, auto&& mid) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        f32x16 sacc[NKB];
+        KVSEL_SETPRIO(1);                  // MFMA issue first; softmax yields to the other wave
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) {
-                sacc[kb2] = f32x16{};
+        for (int kb2 = 0; kb2 < NKB; ++kb2) {          // every S MFMA of the tile is issued first
+            sacc[kb2] = f32x16{};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[buf][(32 * kb2 + krow) * LDK + 16 * ks + 8 * half]);
-                    sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb2], 0, 0, 0);
-                }
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[buf][(32 * kb2 + krow) * LDK + 16 * ks + 8 * half]);
+                sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb2], 0, 0, 0);
             }
-            // register r of block kb2 holds slot s0 + 32*kb2 + 16*(r>>3) + 8*half + (r&7)
-            if (s0 + KT > n_s + w_tmin) {
+        }
+        KVSEL_SETPRIO(0);
+        mid();
+        // Online softmax per 32-key block, so block kb2's softmax overlaps the
+        // MFMAs still running for the next block and its P.V MFMAs overlap the
+        // next block's softmax.
 #pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < NKB; ++kb2) {
+            // this block's V^T fragments are read now so they land during the softmax
+            bf16x8 vf[DB][2];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int sl = s0 + 32 * kb2 + 16 * (r >> 3) + 8 * half + (r & 7);
-                        if (sl > lim) sacc[kb2][r] = -INFINITY;
-                    }
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int k16 = 0; k16 < 2; ++k16)
+                    vf[db][k16] = *reinterpret_cast<const bf16x8*>(&v_lds[buf][(32 * db + col) * LDV + 32 * kb2 + 16 * k16 + 8 * half]);
+            // register r holds slot s0 + 32*kb2 + 16*(r>>3) + 8*half + (r&7)
+            if (MASK) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int sl = s0 + 32 * kb2 + 16 * (r >> 3) + 8 * half + (r & 7);
+                    if (sl > lim) sacc[kb2][r] = -INFINITY;
+                }
             }
             float mt = -INFINITY;
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb2][r]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb2][r]);
+            mt = half_max(mt);
             const float m_new = fmaxf(m, mt);
-            if (__ballot(m_new > m) != 0ull) {
+            if (__ballot((m_new - m) * cl2 > 8.0f) != 0ull) {
                 const float alpha = __builtin_amdgcn_exp2f((m - m_new) * cl2);
                 l *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+                m = m_new;
             }
-            m = m_new;
             const float mc = m * cl2;
-            bf16x8 pf[2][2];
+            bf16x8 pf[2];
+            KVSEL_SETPRIO(0);
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
+            for (int k16 = 0; k16 < 2; ++k16) {
+                u32x4 w;
 #pragma unroll
-                for (int k16 = 0; k16 < 2; ++k16) {
-                    u32x4 w;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e], cl2, -mc));
-                        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e + 1], cl2, -mc));
-                        l += p0 + p1;
-                        w[e] = pack_bf16x2(p0, p1);
-                    }
-                    pf[kb2][k16] = __builtin_bit_cast(bf16x8, w);
+                for (int e = 0; e < 4; ++e) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e], cl2, -mc));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e + 1], cl2, -mc));
+                    l += p0 + p1;
+                    w[e] = pack_bf16x2(p0, p1);
                 }
+                pf[k16] = __builtin_bit_cast(bf16x8, w);
+            }
+            KVSEL_SETPRIO(1);
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                    for (int k16 = 0; k16 < 2; ++k16) {
-                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&v_lds[buf][(32 * db + col) * LDV + 32 * kb2 + 16 * k16 + 8 * half]);
-                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb2][k16], o[db], 0, 0, 0);
-                    }
+                for (int k16 = 0; k16 < 2; ++k16)
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][k16], pf[k16], o[db], 0, 0, 0);
+            KVSEL_SETPRIO(0);
         }
-        if (t + 1 < ntiles) stash(buf ^ 1);
+    };
+
+    fetch_k(0);
+    stash_k(0);
+    fetch_v(0);
+    stash_v(0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        const bool more = t + 1 < ntiles;
+        if (more) fetch_k(t + 1);
+        auto mid = [&] {
+            if (more) {
+                stash_k(buf ^ 1);
+                fetch_v(t + 1);
+            }
+        };
+        const int s0 = t * KT;
+        if (wave_active && s0 <= n_s + w_tmax) {
+            if (s0 + KT > n_s + w_tmin + 1) tile(buf, s0, std::true_type{}, mid);
+            else tile(buf, s0, std::false_type{}, mid);
+        } else {
+            mid();
+        }
+        if (more) stash_v(buf ^ 1);
         __syncthreads();
     }
 
-    l += __shfl_xor(l, 32, kWave);
+    l = half_sum(l);
     if (!rvalid) return;
     const float inv = 1.0f / l;
     // O^T tile: register r of block db holds d = 32*db + 8*(r>>2) + 4*half + (r&3)
@@ -297,11 +356,11 @@ hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const
         const float cl2 = scale * 1.4426950408889634f;
         const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)kall, *vv = (const uint16_t*)vall;
         if (s.d == 128) {
-            if (out_f32) hipLaunchKernelGGL((attn_mfma_kernel<128, true>), grid, dim3(256), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out);
-            else hipLaunchKernelGGL((attn_mfma_kernel<128, false>), grid, dim3(256), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out);
+            if (out_f32) hipLaunchKernelGGL((attn_mfma_kernel<128, true, KVSEL_ATTN_KT>), grid, dim3(256), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out);
+            else hipLaunchKernelGGL((attn_mfma_kernel<128, false, KVSEL_ATTN_KT>), grid, dim3(256), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out);
         } else {
-            if (out_f32) hipLaunchKernelGGL((attn_mfma_kernel<64, true>), grid, dim3(256), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out);
-            else hipLaunchKernelGGL((attn_mfma_kernel<64, false>), grid, dim3(256), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out);
+            if (out_f32) hipLaunchKernelGGL((attn_mfma_kernel<64, true, KVSEL_ATTN_KT>), grid, dim3(256), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out);
+            else hipLaunchKernelGGL((attn_mfma_kernel<64, false, KVSEL_ATTN_KT>), grid, dim3(256), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out);
         }
     } else {
         const float *qq = (const float*)q, *kk = (const float*)kall, *vv = (const float*)vall;

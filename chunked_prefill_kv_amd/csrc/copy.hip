@@ -13,8 +13,6 @@
 
 namespace kvsel {
 
-namespace {
-
 constexpr int kTile = 64;   // slots per workgroup
 
 struct PackArgs {
@@ -33,6 +31,7 @@ struct PackArgs {
     char* kall;
     char* vall;
     int32_t* nsel_out;
+    bool append;             // also write the chunk's rows into the cache at [T_b, T_b + C)
 };
 
 // Source rows of slot s (nullptr = zero row).
@@ -89,6 +88,11 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(PackArgs a) {
         const int64_t dst = (static_cast<int64_t>(bg) * a.nk_pad + s) * a.row_bytes;
         reinterpret_cast<u32x4*>(a.kall + dst)[c] = kv;
         reinterpret_cast<u32x4*>(a.vall + dst)[c] = vv;
+        if (a.append && s >= nsel_b && s < nsel_b + a.C) {
+            const int64_t off = a.cv.row_offset(b, g, T + (s - nsel_b));
+            reinterpret_cast<u32x4*>(a.cv.k + off)[c] = kv;
+            reinterpret_cast<u32x4*>(a.cv.v + off)[c] = vv;
+        }
     }
 }
 
@@ -103,16 +107,30 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(PackArgs a) {
     int64_t T;
     const int nsel_b = seq_nsel(a, b, &T);
     if (a.nsel_out && g == 0 && tile == 0 && threadIdx.x == 0) a.nsel_out[b] = nsel_b;
-    for (int p = threadIdx.x; p < kTile * PPR; p += 256) {
+    constexpr int PPT = kTile * PPR / 256;
+    u32x4 kv[PPT], vv[PPT];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {              // every load in flight before the first store
+        const int p = threadIdx.x + 256 * i;
+        const int r = p / PPR, c = p % PPR;
+        const char *kp, *vp;
+        slot_source(a, b, g, tile * kTile + r, nsel_b, T, &kp, &vp);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        kv[i] = kp ? reinterpret_cast<const u32x4*>(kp)[c] : z;
+        vv[i] = vp ? reinterpret_cast<const u32x4*>(vp)[c] : z;
+    }
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int p = threadIdx.x + 256 * i;
         const int r = p / PPR, c = p % PPR;
         const int s = tile * kTile + r;
-        const char *kp, *vp;
-        slot_source(a, b, g, s, nsel_b, T, &kp, &vp);
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        const u32x4 kv = kp ? reinterpret_cast<const u32x4*>(kp)[c] : z;
-        const u32x4 vv = vp ? reinterpret_cast<const u32x4*>(vp)[c] : z;
-        reinterpret_cast<u32x4*>(a.kall + (static_cast<int64_t>(bg) * a.nk_pad + s) * (D * 2))[c] = kv;
-        *reinterpret_cast<u32x4*>(&vt[r * LDV + c * 8]) = vv;
+        reinterpret_cast<u32x4*>(a.kall + (static_cast<int64_t>(bg) * a.nk_pad + s) * (D * 2))[c] = kv[i];
+        *reinterpret_cast<u32x4*>(&vt[r * LDV + c * 8]) = vv[i];
+        if (a.append && s >= nsel_b && s < nsel_b + a.C) {
+            const int64_t off = a.cv.row_offset(b, g, T + (s - nsel_b));
+            reinterpret_cast<u32x4*>(a.cv.k + off)[c] = kv[i];
+            reinterpret_cast<u32x4*>(a.cv.v + off)[c] = vv[i];
+        }
     }
     __syncthreads();
     // transposed write: thread piece = (d, 8-slot group j)
@@ -151,26 +169,6 @@ __global__ __launch_bounds__(256) void gather_kernel(CacheView cv, const int64_t
     }
 }
 
-// cache rows [T_b, T_b + C) <- the chunk's K/V.
-__global__ __launch_bounds__(256) void append_kernel(CacheView cv, const int64_t* __restrict__ prior_len,
-                                                     const char* __restrict__ k_chunk,
-                                                     const char* __restrict__ v_chunk, int C, int h_kv, int tiles) {
-    const int bg = blockIdx.x / tiles, tile = blockIdx.x % tiles;
-    const int b = bg / h_kv, g = bg % h_kv;
-    const int64_t T = prior_len[b];
-    const int ppr = cv.row_bytes / 16;
-    for (int p = threadIdx.x; p < kTile * ppr; p += 256) {
-        const int t = tile * kTile + p / ppr, c = p % ppr;
-        if (t >= C) continue;
-        const int64_t src = (static_cast<int64_t>(bg) * C + t) * cv.row_bytes;
-        const int64_t off = cv.row_offset(b, g, T + t);
-        reinterpret_cast<u32x4*>(cv.k + off)[c] = reinterpret_cast<const u32x4*>(k_chunk + src)[c];
-        reinterpret_cast<u32x4*>(cv.v + off)[c] = reinterpret_cast<const u32x4*>(v_chunk + src)[c];
-    }
-}
-
-}  // namespace
-
 hipError_t launch_pack(const SelShape& s, const PackSrc& src, const void* k_chunk, const void* v_chunk, int nk_pad,
                        void* kall, void* vall, int32_t* nsel_out, hipStream_t st) {
     PackArgs a;
@@ -194,6 +192,7 @@ hipError_t launch_pack(const SelShape& s, const PackSrc& src, const void* k_chun
     a.kall = static_cast<char*>(kall);
     a.vall = static_cast<char*>(vall);
     a.nsel_out = nsel_out;
+    a.append = src.append;
     dim3 grid(s.batch * s.h_kv * a.tiles), block(256);
     if (s.esz == 2) {
         if (s.d == 128) hipLaunchKernelGGL(pack_bf16_kernel<128>, grid, block, 0, st, a);
@@ -211,14 +210,6 @@ hipError_t launch_gather(const SelShape& s, const CacheView& cv, const int64_t* 
     if (tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(gather_kernel, dim3(s.batch * s.h_kv * tiles), dim3(256), 0, st, cv, prior_len, s.budget, idx,
                        idx_stride, s.h_kv, tiles, static_cast<char*>(k_sel), static_cast<char*>(v_sel), s.budget);
-    return hipGetLastError();
-}
-
-hipError_t launch_append(const SelShape& s, const CacheView& cv, const int64_t* prior_len, const void* k_chunk,
-                         const void* v_chunk, hipStream_t st) {
-    const int tiles = (s.C + kTile - 1) / kTile;
-    hipLaunchKernelGGL(append_kernel, dim3(s.batch * s.h_kv * tiles), dim3(256), 0, st, cv, prior_len,
-                       static_cast<const char*>(k_chunk), static_cast<const char*>(v_chunk), s.C, s.h_kv, tiles);
     return hipGetLastError();
 }
 

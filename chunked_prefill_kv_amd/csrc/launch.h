@@ -23,8 +23,9 @@ struct SelShape {
 // part: fp64 scratch of qstats_part_elems(s) elements.
 hipError_t launch_qstats(const SelShape& s, const void* q, const int64_t* prior_len, double* part,
                          float* qcos, float* qrn, hipStream_t st);
+constexpr int kQRows = 128;   // query rows per statistics workgroup
 inline int64_t qstats_part_elems(const SelShape& s) {
-    return int64_t(s.batch) * s.h_q * ((s.C + 255) / 256) * s.d;
+    return int64_t(s.batch) * s.h_q * ((s.C + kQRows - 1) / kQRows) * s.d;
 }
 
 // Exact top-k with lower-index tie-break, indices ascending, -1 padded to k.
@@ -54,7 +55,9 @@ hipError_t launch_gather(const SelShape& s, const CacheView& cv, const int64_t* 
 // Compacted key/value layout consumed by the attention kernels:
 //   kall [b][g][nk_pad][d]; vall [b][g][d][nk_pad] (bf16, transposed) or
 //   [b][g][nk_pad][d] (fp32).  Slot s < nsel_b: prior key, s < nsel_b + C: the
-//   chunk's key s - nsel_b, beyond: zeros.
+//   chunk's key s - nsel_b, beyond: zeros.  With src.append the chunk's rows
+//   are also written into the cache (the prior rows it reads are [0, T_b), so
+//   the two never overlap).
 struct PackSrc {
     // prior keys from the cache through idx (compact == nullptr) ...
     const CacheView* cache;
@@ -67,6 +70,8 @@ struct PackSrc {
     const void* v_compact;
     const int32_t* n_sel;
     int n_sel_max;
+    // cache mode only: also append the chunk's rows to the cache at [T_b, T_b + C)
+    bool append;
 };
 hipError_t launch_pack(const SelShape& s, const PackSrc& src, const void* k_chunk, const void* v_chunk,
                        int nk_pad, void* kall, void* vall, int32_t* nsel_out, hipStream_t st);
@@ -75,9 +80,5 @@ hipError_t launch_pack(const SelShape& s, const PackSrc& src, const void* k_chun
 hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const void* vall,
                        const int32_t* nsel, int nk_pad, float scale, void* out, bool out_f32,
                        hipStream_t st);
-
-// Append the chunk's K/V rows at [T_b, T_b + C).
-hipError_t launch_append(const SelShape& s, const CacheView& cv, const int64_t* prior_len,
-                         const void* k_chunk, const void* v_chunk, hipStream_t st);
 
 }  // namespace kvsel

@@ -39,7 +39,6 @@ template <> struct Vec8<float> {      // 8 fp32 = two 16-byte loads
 // accumulated in fp64 (the inputs are exact in fp32), so the selection key
 // carries only its final fp32 rounding.
 
-constexpr int kQRows = 256;   // query rows per workgroup
 
 // pass 1: per (head, row block) column sums of the query rows -> part[bh][blk][D] (fp64)
 template <typename T, int D>
@@ -54,12 +53,18 @@ __global__ __launch_bounds__(256) void qsum_kernel(const T* __restrict__ q, int 
     const int c8 = threadIdx.x % G8, sub = threadIdx.x / G8;
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const int r1 = min(C, (blk + 1) * kQRows);
-    for (int r = blk * kQRows + sub; r < r1; r += RPP) {
-        float x[8];
-        Vec8<T>::load(qh + static_cast<int64_t>(r) * D + c8 * 8, x);
+    constexpr int NIT = kQRows / RPP;
+    float x[NIT][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += static_cast<double>(x[i]);
+    for (int it = 0; it < NIT; ++it) {           // all loads in flight first
+        const int r = blk * kQRows + sub + it * RPP;
+        if (r < r1) Vec8<T>::load(qh + static_cast<int64_t>(r) * D + c8 * 8, x[it]);
+        else for (int i = 0; i < 8; ++i) x[it][i] = 0.0f;
     }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += static_cast<double>(x[it][i]);
     __shared__ double red[RPP][D];
 #pragma unroll
     for (int i = 0; i < 8; ++i) red[sub][c8 * 8 + i] = acc[i];
@@ -85,7 +90,14 @@ __global__ __launch_bounds__(256) void qcos_kernel(const T* __restrict__ q, int 
     __shared__ double mnorm;
     if (threadIdx.x < D) {
         double s = 0.0;
-        for (int k = 0; k < nblk; ++k) s += part[(static_cast<int64_t>(bh) * nblk + k) * D + threadIdx.x];
+        for (int k0 = 0; k0 < nblk; k0 += 8) {          // 8 loads in flight, summed in block order
+            double v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = k0 + i < nblk ? part[(static_cast<int64_t>(bh) * nblk + k0 + i) * D + threadIdx.x] : 0.0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s += v[i];
+        }
         mean[threadIdx.x] = s / C;
     }
     __syncthreads();
@@ -104,18 +116,23 @@ __global__ __launch_bounds__(256) void qcos_kernel(const T* __restrict__ q, int 
     const double mn = mnorm;
     const T* qh = q + static_cast<int64_t>(bh) * C * D;
     const int r1 = min(C, (blk + 1) * kQRows);
-    for (int r0 = blk * kQRows; r0 < r1; r0 += RPP) {      // uniform trip count: shuffles stay converged
-        const int r = r0 + sub;
-        double dot = 0.0, n2 = 0.0;
-        if (r < r1) {
-            float x[8];
-            Vec8<T>::load(qh + static_cast<int64_t>(r) * D + c8 * 8, x);
+    constexpr int NIT = kQRows / RPP;
+    float x[NIT][8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const double xd = x[i];
-                dot += xd * m[i];
-                n2 += xd * xd;
-            }
+    for (int it = 0; it < NIT; ++it) {           // all loads in flight first
+        const int r = blk * kQRows + sub + it * RPP;
+        if (r < r1) Vec8<T>::load(qh + static_cast<int64_t>(r) * D + c8 * 8, x[it]);
+        else for (int i = 0; i < 8; ++i) x[it][i] = 0.0f;
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {           // uniform trip count: shuffles stay converged
+        const int r = blk * kQRows + sub + it * RPP;
+        double dot = 0.0, n2 = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const double xd = x[it][i];
+            dot += xd * m[i];
+            n2 += xd * xd;
         }
 #pragma unroll
         for (int o = G8 / 2; o >= 1; o >>= 1) {               // reduce over the row's lanes
@@ -133,7 +150,10 @@ __global__ __launch_bounds__(256) void qcos_kernel(const T* __restrict__ q, int 
 
 // ----------------------------------------------------------------------------- exact top-k
 
-constexpr int kTopkThreads = 1024;
+#ifndef KVSEL_TOPK_THREADS
+#define KVSEL_TOPK_THREADS 1024
+#endif
+constexpr int kTopkThreads = KVSEL_TOPK_THREADS;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kHistBins = 2048;   // 11-bit digits
 
@@ -160,7 +180,10 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
     return off + incl - v;
 }
 
-constexpr int kLdsKeys = 30720;   // problems up to this size keep their keys in LDS (120 KB)
+#ifndef KVSEL_TOPK_LDS_KEYS
+#define KVSEL_TOPK_LDS_KEYS 30720
+#endif
+constexpr int kLdsKeys = KVSEL_TOPK_LDS_KEYS;   // problems up to this size keep their keys in LDS
 
 template <bool kLds>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores, int64_t score_stride,
@@ -198,10 +221,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     // bits shared by every key need no histogram pass
     const uint32_t first = gkey(0);
     uint32_t diff = 0;
-    for (int j = tid; j < n; j += kTopkThreads) {
-        const uint32_t u = gkey(j);
-        if (kLds) kc[j] = u;
-        diff |= u ^ first;
+    for (int j0 = tid; j0 < n; j0 += 8 * kTopkThreads) {     // 8 independent loads in flight per thread
+        uint32_t u[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = j0 + i * kTopkThreads;
+            u[i] = j < n ? gkey(j) : first;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = j0 + i * kTopkThreads;
+            if (kLds && j < n) kc[j] = u[i];
+            diff |= u[i] ^ first;
+        }
     }
 #pragma unroll
     for (int o2 = 32; o2 >= 1; o2 >>= 1) diff |= __shfl_xor(diff, o2, kWave);
@@ -221,23 +253,36 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
         const uint32_t dmask = (1u << w) - 1u;
         for (int i = tid; i < kHistBins; i += kTopkThreads) hist[i] = 0;
         __syncthreads();
-        for (int j = tid; j < n; j += kTopkThreads) {
-            const uint32_t u = key(j);
-            const bool match = (bits == 32) || ((u >> bits) == (prefix >> bits));
-            if (match) atomicAdd(&hist[(u >> shift) & dmask], 1u);
+        for (int j0 = tid; j0 < n; j0 += 4 * kTopkThreads) {
+            uint32_t u[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = j0 + i * kTopkThreads;
+                u[i] = j < n ? key(j) : 0u;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = j0 + i * kTopkThreads;
+                const bool match = (bits == 32) || ((u[i] >> bits) == (prefix >> bits));
+                if (j < n && match) atomicAdd(&hist[(u[i] >> shift) & dmask], 1u);
+            }
         }
         __syncthreads();
-        // thread t owns bins 2t, 2t+1; counts of all higher bins via a reversed scan
+        // thread t owns bins [BPT*t, BPT*t + BPT); counts of all higher bins via a reversed scan
+        constexpr int BPT = kHistBins / kTopkThreads;
         const int t = kTopkThreads - 1 - tid;               // reversed order
-        const uint32_t h0 = hist[2 * t], h1 = hist[2 * t + 1];
+        uint32_t hb[BPT], hsum = 0;
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) { hb[i] = hist[BPT * t + i]; hsum += hb[i]; }
         uint32_t tot;
-        const uint32_t above = block_excl_scan(h0 + h1, wsum, &tot);   // bins > 2t+1
-        if (above < remaining && above + h1 >= remaining) {
-            s_digit = 2 * t + 1;
-            s_rem = remaining - above;
-        } else if (above + h1 < remaining && above + h1 + h0 >= remaining) {
-            s_digit = 2 * t;
-            s_rem = remaining - above - h1;
+        uint32_t above = block_excl_scan(hsum, wsum, &tot);   // keys in bins above BPT*t + BPT - 1
+#pragma unroll
+        for (int i = BPT - 1; i >= 0; --i) {
+            if (above < remaining && above + hb[i] >= remaining) {
+                s_digit = BPT * t + i;
+                s_rem = remaining - above;
+            }
+            above += hb[i];
         }
         __syncthreads();
         prefix |= s_digit << shift;
@@ -248,39 +293,42 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     const uint32_t tau = prefix;          // the k-th largest key
     const uint32_t need = remaining;      // keys equal to tau that are kept (lowest indices)
 
+    // Ordered compaction: wave w owns the contiguous segment [w*seg, (w+1)*seg).
+    // Pass 1 counts keys above tau and equal to tau per wave; after one barrier
+    // every wave knows how many of each precede its segment, and pass 2 writes
+    // each kept index at (#above before it) + min(#equal before it, need).
     const uint64_t lt = (1ull << lane) - 1ull;
-    uint32_t eq_before = 0, sel_before = 0;
-    for (int base = 0; base < n && sel_before < static_cast<uint32_t>(k); base += kTopkThreads) {
-        const int j = base + tid;
-        const uint32_t u = j < n ? key(j) : 0u;
-        const bool gt = j < n && u > tau;
-        const bool eq = j < n && u == tau;
-        const uint64_t be = __ballot(eq);
-        if (lane == 0) wtot[0][wave] = __popcll(be);
-        __syncthreads();
-        uint32_t off_eq = 0, tot_eq = 0;
-#pragma unroll
-        for (int w = 0; w < kTopkWaves; ++w) {
-            const uint32_t s = wtot[0][w];
-            off_eq += (w < wave) ? s : 0u;
-            tot_eq += s;
-        }
-        const uint32_t eq_rank = eq_before + off_eq + __popcll(be & lt);
-        const bool sel = gt || (eq && eq_rank < need);
-        const uint64_t bs = __ballot(sel);
-        if (lane == 0) wtot[1][wave] = __popcll(bs);
-        __syncthreads();
-        uint32_t off_sel = 0, tot_sel = 0;
-#pragma unroll
-        for (int w = 0; w < kTopkWaves; ++w) {
-            const uint32_t s = wtot[1][w];
-            off_sel += (w < wave) ? s : 0u;
-            tot_sel += s;
-        }
-        if (sel) o[sel_before + off_sel + __popcll(bs & lt)] = j;
-        eq_before += tot_eq;
-        sel_before += tot_sel;
-        __syncthreads();
+    const int seg = ((n + kTopkWaves - 1) / kTopkWaves + kWave - 1) / kWave * kWave;
+    const int j0 = wave * seg, j1 = min(n, j0 + seg);
+    uint32_t n_gt = 0, n_eq = 0;
+    for (int base = j0; base < j1; base += kWave) {
+        const int j = base + lane;
+        const uint32_t u = j < j1 ? key(j) : 0u;
+        n_gt += __popcll(__ballot(j < j1 && u > tau));
+        n_eq += __popcll(__ballot(j < j1 && u == tau));
+    }
+    if (lane == 0) {
+        wtot[0][wave] = n_gt;
+        wtot[1][wave] = n_eq;
+    }
+    __syncthreads();
+    uint32_t gt_run = 0, eq_run = 0;
+    for (int w = 0; w < wave; ++w) {
+        gt_run += wtot[0][w];
+        eq_run += wtot[1][w];
+    }
+    for (int base = j0; base < j1 && gt_run + min(eq_run, need) < static_cast<uint32_t>(k); base += kWave) {
+        const int j = base + lane;
+        const uint32_t u = j < j1 ? key(j) : 0u;
+        const bool gt = j < j1 && u > tau;
+        const bool eq = j < j1 && u == tau;
+        const uint64_t bgt = __ballot(gt), beq = __ballot(eq);
+        const uint32_t gt_before = gt_run + __popcll(bgt & lt);
+        const uint32_t eq_before = eq_run + __popcll(beq & lt);
+        if (gt) o[gt_before + min(eq_before, need)] = j;
+        else if (eq && eq_before < need) o[gt_before + eq_before] = j;
+        gt_run += __popcll(bgt);
+        eq_run += __popcll(beq);
     }
 }
 
@@ -288,25 +336,41 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pack_qsel_kernel(const T* __restrict__ q, int h_q, int G, int C, int nqp,
-                                                        int nq_pad, const int32_t* __restrict__ keep,
+                                                        int nq_pad, int rblocks, const int32_t* __restrict__ keep,
                                                         int64_t keep_stride, const float* __restrict__ qrn,
                                                         const int64_t* __restrict__ prior_len, int64_t budget,
                                                         T* __restrict__ qsel, float* __restrict__ rq) {
-    const int bh = blockIdx.x;
+    constexpr int kPieces = D * sizeof(T) / 16;          // 16-byte pieces per row
+    constexpr int kRows = 32;                            // rows per workgroup
+    constexpr int PPT = kRows * kPieces / 256;           // pieces per thread
+    const int bh = blockIdx.x / rblocks, rb = blockIdx.x % rblocks;
     const int b = bh / h_q, h = bh % h_q;
     if (prior_len[b] <= budget) return;
     const int g = h / G, hh = h % G;
     const int h_kv = h_q / G;
-    constexpr int kPieces = D * sizeof(T) / 16;          // 16-byte pieces per row
     const int64_t dst_row0 = (static_cast<int64_t>(b) * h_kv + g) * G * nq_pad + static_cast<int64_t>(hh) * nq_pad;
     const int32_t* kp = keep + static_cast<int64_t>(bh) * keep_stride;
-    for (int i = threadIdx.x; i < nq_pad * kPieces; i += 256) {
-        const int r = i / kPieces, pc = i % kPieces;
-        const int t = kp[r < nqp ? r : 0];
-        const u32x4* src = reinterpret_cast<const u32x4*>(q + (static_cast<int64_t>(bh) * C + t) * D) + pc;
-        u32x4* dst = reinterpret_cast<u32x4*>(qsel + (dst_row0 + r) * D) + pc;
-        *dst = *src;
-        if (pc == 0) rq[dst_row0 + r] = qrn[static_cast<int64_t>(bh) * C + t];
+    u32x4 v[PPT];
+    int rr[PPT];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int p = threadIdx.x + 256 * i;
+        const int r = rb * kRows + p / kPieces, pc = p % kPieces;
+        rr[i] = r;
+        if (r < nq_pad) {
+            const int t = kp[r < nqp ? r : 0];
+            v[i] = reinterpret_cast<const u32x4*>(q + (static_cast<int64_t>(bh) * C + t) * D)[pc];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int p = threadIdx.x + 256 * i;
+        const int r = rr[i], pc = p % kPieces;
+        if (r < nq_pad) reinterpret_cast<u32x4*>(qsel + (dst_row0 + r) * D)[pc] = v[i];
+    }
+    if (threadIdx.x < kRows) {
+        const int r = rb * kRows + threadIdx.x;
+        if (r < nq_pad) rq[dst_row0 + r] = qrn[static_cast<int64_t>(bh) * C + kp[r < nqp ? r : 0]];
     }
 }
 
@@ -348,13 +412,14 @@ hipError_t launch_topk(int problems, int heads_per_seq, const float* scores, int
 
 hipError_t launch_pack_qsel(const SelShape& s, const void* q, const int32_t* keep, int64_t keep_stride,
                             const float* qrn, const int64_t* prior_len, void* qsel, float* rq, hipStream_t st) {
-    dim3 grid(s.batch * s.h_q), block(256);
+    const int rblocks = (s.nq_pad + 31) / 32;
+    dim3 grid(s.batch * s.h_q * rblocks), block(256);
     if (s.esz == 2) {
-        if (s.d == 128) hipLaunchKernelGGL((pack_qsel_kernel<uint16_t, 128>), grid, block, 0, st, (const uint16_t*)q, s.h_q, s.G, s.C, s.nqp, s.nq_pad, keep, keep_stride, qrn, prior_len, s.budget, (uint16_t*)qsel, rq);
-        else hipLaunchKernelGGL((pack_qsel_kernel<uint16_t, 64>), grid, block, 0, st, (const uint16_t*)q, s.h_q, s.G, s.C, s.nqp, s.nq_pad, keep, keep_stride, qrn, prior_len, s.budget, (uint16_t*)qsel, rq);
+        if (s.d == 128) hipLaunchKernelGGL((pack_qsel_kernel<uint16_t, 128>), grid, block, 0, st, (const uint16_t*)q, s.h_q, s.G, s.C, s.nqp, s.nq_pad, rblocks, keep, keep_stride, qrn, prior_len, s.budget, (uint16_t*)qsel, rq);
+        else hipLaunchKernelGGL((pack_qsel_kernel<uint16_t, 64>), grid, block, 0, st, (const uint16_t*)q, s.h_q, s.G, s.C, s.nqp, s.nq_pad, rblocks, keep, keep_stride, qrn, prior_len, s.budget, (uint16_t*)qsel, rq);
     } else {
-        if (s.d == 128) hipLaunchKernelGGL((pack_qsel_kernel<float, 128>), grid, block, 0, st, (const float*)q, s.h_q, s.G, s.C, s.nqp, s.nq_pad, keep, keep_stride, qrn, prior_len, s.budget, (float*)qsel, rq);
-        else hipLaunchKernelGGL((pack_qsel_kernel<float, 64>), grid, block, 0, st, (const float*)q, s.h_q, s.G, s.C, s.nqp, s.nq_pad, keep, keep_stride, qrn, prior_len, s.budget, (float*)qsel, rq);
+        if (s.d == 128) hipLaunchKernelGGL((pack_qsel_kernel<float, 128>), grid, block, 0, st, (const float*)q, s.h_q, s.G, s.C, s.nqp, s.nq_pad, rblocks, keep, keep_stride, qrn, prior_len, s.budget, (float*)qsel, rq);
+        else hipLaunchKernelGGL((pack_qsel_kernel<float, 64>), grid, block, 0, st, (const float*)q, s.h_q, s.G, s.C, s.nqp, s.nq_pad, rblocks, keep, keep_stride, qrn, prior_len, s.budget, (float*)qsel, rq);
     }
     return hipGetLastError();
 }

@@ -166,9 +166,9 @@ typedef enum {
     KVSEL_K_SCAN = 3,     /* step 2: cosine key scores over the prior cache */
     KVSEL_K_TOPB = 4,     /* step 3: per-KV-head top-B */
     KVSEL_K_GATHER = 5,   /* step 4 (kvsel_select): k_sel/v_sel rows */
-    KVSEL_K_PACK = 6,     /* step 4: compacted keys + chunk keys for attention */
+    KVSEL_K_PACK = 6,     /* step 4: compacted keys + chunk keys for attention, and the cache append */
     KVSEL_K_ATTN = 7,     /* step 5: attention */
-    KVSEL_K_APPEND = 8,   /* cache append */
+    KVSEL_K_APPEND = 8,   /* reserved: the cache append runs inside the pack kernel */
     KVSEL_K_COUNT = 9
 } kvsel_kernel;
 
