@@ -87,6 +87,8 @@ def main():
     ap.add_argument("--workload", default="llama8b_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--lib", default=None, help="path of an alternative libkvsel.so build")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (the reference kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the kernels shard by KV head "
@@ -96,6 +98,18 @@ def main():
     import torch
     from chunked_prefill_kv_amd import gen, runner
     from chunked_prefill_kv_amd import kvsel as K
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+    if gen.WORKLOADS[args.workload].L == 0:
+        return bench_decode(args)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     K.load(args.lib) if args.lib else K.load()
@@ -163,6 +177,51 @@ def main():
         out["cpu_baseline"] = cpu_baseline(wl, chunks)
     else:
         out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(args):
+    """One ragged paged decode step (chunk of 1 per sequence) of the decode workload."""
+    import torch
+    from chunked_prefill_kv_amd import gen, runner
+    from chunked_prefill_kv_amd import kvsel as K
+    K.load(args.lib) if args.lib else K.load()
+    wl = gen.WORKLOADS[args.workload]
+    print(f"[bench] generating {wl.name} inputs", file=sys.stderr, flush=True)
+    di = gen.decode_inputs(wl)
+    dr = runner.DecodeRunner(wl, di, out_dtype=torch.bfloat16)
+    for _ in range(args.warmup):
+        dr.run()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(args.steps):
+        dr.run()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    K.trace_start()
+    for _ in range(args.steps):
+        dr.run()
+    torch.cuda.synchronize()
+    K.trace_stop()
+    tr = K.trace_read()
+    T = di.prior_len.astype(np.float64)
+    scan_bytes = float((T[T > wl.B] * wl.H_kv * wl.d * 2).sum())      # every prior key read once
+    n_sc, ms_sc = tr.get("scan", (1, float("nan")))
+    gbs = scan_bytes * args.steps / (ms_sc * 1e-3) / 1e9
+    out = {"metric": "decode tokens/s/layer (select+attend), ragged paged batch", "value": round(wl.batch / (ms_step / 1e3), 1),
+           "unit": "tokens/s/layer", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": wl.name, "batch": wl.batch, "prior_len_mean": float(T.mean()), "B": wl.B,
+                      "H_q": wl.H_q, "H_kv": wl.H_kv, "d": wl.d, "block_size": wl.block_size},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "scan (one query per head)",
+                        "launches": n_sc, "avg_launch_us": round(ms_sc * 1e3 / n_sc, 2)},
+           "kernels": {k: {"ms_per_step": round(v[1] / args.steps, 4)} for k, v in tr.items()},
+           "cpu_baseline": None}
     print(json.dumps(out), flush=True)
 
 

@@ -169,13 +169,14 @@ SelShape make_shape(const kvsel_heads* h, const kvsel_batch* b, const kvsel_para
     else s.nq_pad = static_cast<int>(round_up(s.nqp, 32));                // MFMA scan: 32-row blocks
     s.budget = p ? p->budget : 0;
     s.t_max = t_max;
+    s.nsplit = (s.esz == 2 && s.nq_pad % 32 == 0) ? scan_splits(s.batch, s.h_kv, s.G, t_max) : 1;
     return s;
 }
 
 // ----------------------------------------------------------------------------- workspace layout
 
 struct Layout {
-    size_t qpart, qcos, qrn, keep, qsel, rq, scores, idx, nsel, kall, vall, total;
+    size_t qpart, qcos, qrn, keep, qsel, rq, scores, topb, idx, nsel, kall, vall, total;
     int nk_pad;
 };
 
@@ -190,7 +191,8 @@ Layout layout(const SelShape& s, bool with_attn) {
     L.keep = take(bh * s.nqp * 4);
     L.qsel = take(bg * s.G * s.nq_pad * s.d * s.esz);
     L.rq = take(bg * s.G * s.nq_pad * 4);
-    L.scores = take(bg * (s.t_max > 0 ? s.t_max : 1) * 4);
+    L.scores = take(bg * (s.t_max > 0 ? s.t_max : 1) * 4 * s.nsplit);
+    L.topb = take(topb_scratch_bytes(static_cast<int>(bg), s.t_max, s.budget));
     L.idx = take(bg * s.budget * 4);
     L.nsel = take(size_t(s.batch) * 4);
     const int64_t nsel_max = s.budget < s.t_max ? s.budget : s.t_max;
@@ -218,18 +220,22 @@ kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, 
     bool any = false;
     for (int i = 0; i < b->batch; ++i) any |= b->prior_len_host[i] > s.budget;
     const int64_t* T = b->prior_len_dev;
-    float* S = scores ? scores : at<float>(ws, L.scores);
+    // the scan writes into the workspace (its split partials when s.nsplit > 1);
+    // the top-B kernel adds the splits and stores the sum in `scores` if asked
+    float* S = (scores && s.nsplit == 1) ? scores : at<float>(ws, L.scores);
+    const int64_t split_stride = int64_t(s.batch) * s.h_kv * s.t_max;
     if (any) {
         int32_t* keep = q_keep ? q_keep : at<int32_t>(ws, L.keep);
-        KVSEL_TRY(traced(KVSEL_K_QSTATS, st, [&] { return launch_qstats(s, q, T, at<double>(ws, L.qpart), at<float>(ws, L.qcos), at<float>(ws, L.qrn), st); }), "query statistics");
-        KVSEL_TRY(traced(KVSEL_K_QTOPK, st, [&] { return launch_topk(s.batch * s.h_q, s.h_q, at<float>(ws, L.qcos), s.C, T, s.C, s.budget, s.nqp, keep, s.nqp,
+        KVSEL_TRY(traced(KVSEL_K_QSTATS, st, [&] { return launch_qstats(s, q, T, at<double>(ws, L.qpart), at<float>(ws, L.qcos), at<float>(ws, L.qrn), at<uint32_t>(ws, L.topb), int64_t(s.batch) * s.h_kv * 4096, st); }), "query statistics");
+        KVSEL_TRY(traced(KVSEL_K_QTOPK, st, [&] { return launch_topk(s.batch * s.h_q, s.h_q, at<float>(ws, L.qcos), s.C, 1, 0, nullptr, T, s.C, s.budget, s.nqp, keep, s.nqp,
                               1, s.C, st); }), "query top-k");
         KVSEL_TRY(traced(KVSEL_K_QPACK, st, [&] { return launch_pack_qsel(s, q, keep, s.nqp, at<float>(ws, L.qrn), T, at<void>(ws, L.qsel), at<float>(ws, L.rq), st); }),
                   "query packing");
         KVSEL_TRY(traced(KVSEL_K_SCAN, st, [&] { return launch_scan(s, at<void>(ws, L.qsel), at<float>(ws, L.rq), cv, T, S, s.t_max, st); }), "key scan");
     }
-    KVSEL_TRY(traced(KVSEL_K_TOPB, st, [&] { return launch_topk(s.batch * s.h_kv, s.h_kv, S, s.t_max, T, 0, s.budget, static_cast<int>(s.budget), idx,
-                          s.budget, 0, s.t_max, st); }), "key top-B");
+    float* comb = scores ? scores : S;
+    KVSEL_TRY(traced(KVSEL_K_TOPB, st, [&] { return launch_topb(s.batch * s.h_kv, s.h_kv, S, s.nsplit, split_stride, comb, s.t_max, T,
+                                                                s.budget, s.t_max, any, at<uint32_t>(ws, L.topb), idx, st); }), "key top-B");
     return KVSEL_OK;
 }
 

@@ -16,13 +16,25 @@ struct SelShape {
     int nq_pad;                       // rows reserved per head in Q_sel (>= nqp)
     int64_t budget;
     int64_t t_max;                    // max_b T_b
+    int nsplit;                       // MFMA scan: query-head groups per key tile (1 = no split)
 };
+
+// Choose how many query-head groups the MFMA scan splits a KV head into: a
+// power of two dividing G (at most 8), the smallest that gives >= 512
+// workgroups for the largest prior length.
+inline int scan_splits(int batch, int h_kv, int G, int64_t t_max) {
+    const int64_t tiles = (t_max + 255) / 256;
+    int ns = 1;
+    while (ns < 8 && G % (2 * ns) == 0 && int64_t(batch) * h_kv * tiles * ns < 512) ns *= 2;
+    return ns;
+}
 
 // Step 1: per (b, h) cosine of each chunk query to the mean query (selection
 // key) and 1/|q| of each query.  Sequences with T_b <= budget are skipped.
-// part: fp64 scratch of qstats_part_elems(s) elements.
+// part: fp64 scratch of qstats_part_elems(s) elements.  The first pass also
+// clears zero[0..zero_n) (the top-B histogram) for the kernels that follow.
 hipError_t launch_qstats(const SelShape& s, const void* q, const int64_t* prior_len, double* part,
-                         float* qcos, float* qrn, hipStream_t st);
+                         float* qcos, float* qrn, uint32_t* zero, int64_t zero_n, hipStream_t st);
 constexpr int kQRows = 128;   // query rows per statistics workgroup
 inline int64_t qstats_part_elems(const SelShape& s) {
     return int64_t(s.batch) * s.h_q * ((s.C + kQRows - 1) / kQRows) * s.d;
@@ -33,9 +45,25 @@ inline int64_t qstats_part_elems(const SelShape& s) {
 //   mode 1: the k smallest of scores[p][0..n_fixed) (query keep); problems
 //           whose sequence has T_b <= budget are skipped
 // When n_p <= k every index [0, n_p) is taken.  max_n bounds every n_p.
+// The score of key j is the sum, in split order, of nsplit partial arrays
+// scores + s * split_stride; when s_out is given that sum is also stored there
+// (same indexing as scores).
 hipError_t launch_topk(int problems, int heads_per_seq, const float* scores, int64_t score_stride,
+                       int nsplit, int64_t split_stride, float* s_out,
                        const int64_t* prior_len, int n_fixed, int64_t budget, int k,
                        int32_t* out, int64_t out_stride, int mode, int64_t max_n, hipStream_t st);
+
+// Per-KV-head top-B of the (split-partial) key scores on many workgroups:
+// writes out[p][0..budget) (kept indices ascending, -1 past T_p) for every
+// problem p = b * heads_per_seq + g.  comb receives the summed scores (may be
+// `part` itself).  scratch: topb_scratch_bytes(); its histogram part
+// (problems * 4096 uint32 at its start) must be zero on entry when
+// any_select (launch_qstats clears it).
+int topb_segments(int64_t t_max, int64_t budget);
+size_t topb_scratch_bytes(int problems, int64_t t_max, int64_t budget);
+hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int nsplit, int64_t split_stride,
+                       float* comb, int64_t s_stride, const int64_t* prior_len, int64_t budget, int64_t t_max,
+                       bool any_select, uint32_t* scratch, int32_t* out, hipStream_t st);
 
 // Gather the kept query rows of every head into Q_sel[b][g][hh*nq_pad + r][d]
 // (raw rows) and rq = 1/|q|; rows r >= nqp repeat row 0 of that head.
@@ -43,7 +71,9 @@ hipError_t launch_pack_qsel(const SelShape& s, const void* q, const int32_t* kee
                             const float* qrn, const int64_t* prior_len, void* qsel, float* rq,
                             hipStream_t st);
 
-// Step 2: S[b][g][j] for j < T_b (sequences with T_b > budget only).
+// Step 2: S[b][g][j] for j < T_b (sequences with T_b > budget only).  With
+// s.nsplit > 1 the MFMA scan writes s.nsplit partial arrays, split k at
+// S + k * (batch * h_kv * s_stride), whose sum is the score.
 hipError_t launch_scan(const SelShape& s, const void* qsel, const float* rq, const CacheView& cv,
                        const int64_t* prior_len, float* S, int64_t s_stride, hipStream_t st);
 

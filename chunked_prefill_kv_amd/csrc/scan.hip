@@ -21,12 +21,18 @@ namespace kvsel {
 // MFMA result tile has queries on rows and keys on columns, so each lane holds
 // 16 query rows of one key: the max over queries is in-register plus one
 // exchange between the two half-waves at the end of every head.
+//
+// The G query heads may be split over `nsplit` workgroups per key tile (more
+// workgroups when the cache or the KV head count is small); split s writes
+// the sum over its heads, scaled by 1/G, to S + s * split_stride and the top-B
+// kernel adds the splits in order.
 template <int D, int NB>
 __global__ __launch_bounds__(256, 2) void scan_mfma_kernel(const uint16_t* __restrict__ qsel,
                                                            const float* __restrict__ rq, CacheView cv,
                                                            const int64_t* __restrict__ prior_len, int64_t budget,
-                                                           int h_kv, int G, int nq_pad, int tiles,
-                                                           float* __restrict__ S, int64_t s_stride) {
+                                                           int h_kv, int G, int nq_pad, int tiles, int nsplit,
+                                                           float* __restrict__ S, int64_t s_stride,
+                                                           int64_t split_stride) {
     constexpr int KS = D / 16;              // MFMA k-steps over the head dim
     constexpr int KEYS = 4 * NB * 32;       // keys per workgroup
     constexpr int STAGE = 64;               // query rows per LDS stage
@@ -37,7 +43,9 @@ __global__ __launch_bounds__(256, 2) void scan_mfma_kernel(const uint16_t* __res
     __shared__ __attribute__((aligned(16))) float rqs[2][STAGE];
 
     const int slot = xcd_slot(blockIdx.x, gridDim.x);
-    const int bg = slot / tiles, tile = slot % tiles;
+    const int tile = slot % tiles;
+    const int split = (slot / tiles) % nsplit;
+    const int bg = slot / tiles / nsplit;
     const int b = bg / h_kv, g = bg % h_kv;
     const int64_t T = prior_len[b];
     if (T <= budget) return;
@@ -72,10 +80,10 @@ __global__ __launch_bounds__(256, 2) void scan_mfma_kernel(const uint16_t* __res
         rk[kb] = n2 > 0.0f ? 1.0f / sqrtf(n2) : 0.0f;
     }
 
-    const int R = G * nq_pad;
+    const int R = G / nsplit * nq_pad;                  // this split's query rows
     const int nstage = (R + STAGE - 1) / STAGE;
-    const uint16_t* qb = qsel + static_cast<int64_t>(bg) * R * D;
-    const float* rqb = rq + static_cast<int64_t>(bg) * R;
+    const uint16_t* qb = qsel + (static_cast<int64_t>(bg) * G * nq_pad + static_cast<int64_t>(split) * R) * D;
+    const float* rqb = rq + static_cast<int64_t>(bg) * G * nq_pad + static_cast<int64_t>(split) * R;
 
     u32x4 pre[PPT];
     float prq = 0.0f;
@@ -153,7 +161,7 @@ __global__ __launch_bounds__(256, 2) void scan_mfma_kernel(const uint16_t* __res
     }
 
     const float inv_g = 1.0f / static_cast<float>(G);
-    float* Sb = S + static_cast<int64_t>(bg) * s_stride;
+    float* Sb = S + static_cast<int64_t>(split) * split_stride + static_cast<int64_t>(bg) * s_stride;
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) {
         const int64_t key = key0 + (wave * NB + kb) * 32 + col;
@@ -306,9 +314,10 @@ hipError_t launch_scan(const SelShape& s, const void* qsel, const float* rq, con
     } else if (s.esz == 2) {
         constexpr int NB = 2;
         const int tiles = static_cast<int>((s.t_max + 4 * NB * 32 - 1) / (4 * NB * 32));
-        dim3 grid(bgs * tiles), block(256);
-        if (s.d == 128) hipLaunchKernelGGL((scan_mfma_kernel<128, NB>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, S, s_stride);
-        else hipLaunchKernelGGL((scan_mfma_kernel<64, NB>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, S, s_stride);
+        dim3 grid(bgs * tiles * s.nsplit), block(256);
+        const int64_t split_stride = int64_t(bgs) * s_stride;
+        if (s.d == 128) hipLaunchKernelGGL((scan_mfma_kernel<128, NB>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, s.nsplit, S, s_stride, split_stride);
+        else hipLaunchKernelGGL((scan_mfma_kernel<64, NB>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, s.nsplit, S, s_stride, split_stride);
     } else {
         const int tiles = static_cast<int>((s.t_max + 255) / 256);
         dim3 grid(bgs * tiles), block(256);

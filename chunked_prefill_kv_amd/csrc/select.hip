@@ -44,9 +44,11 @@ template <> struct Vec8<float> {      // 8 fp32 = two 16-byte loads
 template <typename T, int D>
 __global__ __launch_bounds__(256) void qsum_kernel(const T* __restrict__ q, int h_q, int C, int nblk,
                                                    const int64_t* __restrict__ prior_len, int64_t budget,
-                                                   double* __restrict__ part) {
+                                                   double* __restrict__ part, uint32_t* __restrict__ zero,
+                                                   int64_t zero_n) {
     constexpr int G8 = D / 8;                 // 8-column groups per row
     constexpr int RPP = 256 / G8;             // rows per pass
+    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < zero_n; i += int64_t(gridDim.x) * 256) zero[i] = 0;
     const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
     if (prior_len[bh / h_q] <= budget) return;
     const T* qh = q + static_cast<int64_t>(bh) * C * D;
@@ -187,6 +189,7 @@ constexpr int kLdsKeys = KVSEL_TOPK_LDS_KEYS;   // problems up to this size keep
 
 template <bool kLds>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores, int64_t score_stride,
+                                                            int nsplit, int64_t split_stride, float* __restrict__ s_out,
                                                             int heads_per_seq, const int64_t* __restrict__ prior_len,
                                                             int n_fixed, int64_t budget, int k,
                                                             int32_t* __restrict__ out, int64_t out_stride, int mode) {
@@ -210,7 +213,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     }
     const uint32_t flip = mode ? 0xFFFFFFFFu : 0u;   // mode 1 keeps the smallest
     __shared__ uint32_t kc[kLds ? kLdsKeys : 1];      // the problem's order keys when they fit
-    auto gkey = [&](int j) -> uint32_t { return order_key(x[j]) ^ flip; };
+    auto gval = [&](int j) -> float {                  // partial scores summed in split order
+        float v = x[j];
+        for (int sp = 1; sp < nsplit; ++sp) v += x[j + sp * split_stride];
+        return v;
+    };
+    auto gkey = [&](int j) -> uint32_t { return order_key(gval(j)) ^ flip; };
+    float* so = s_out ? s_out + static_cast<int64_t>(p) * score_stride : nullptr;
     auto key = [&](int j) -> uint32_t { return kLds ? kc[j] : gkey(j); };
 
     __shared__ uint32_t hist[kHistBins];
@@ -222,17 +231,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     const uint32_t first = gkey(0);
     uint32_t diff = 0;
     for (int j0 = tid; j0 < n; j0 += 8 * kTopkThreads) {     // 8 independent loads in flight per thread
-        uint32_t u[8];
+        float v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int j = j0 + i * kTopkThreads;
-            u[i] = j < n ? gkey(j) : first;
+            v[i] = j < n ? gval(j) : 0.0f;
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int j = j0 + i * kTopkThreads;
-            if (kLds && j < n) kc[j] = u[i];
-            diff |= u[i] ^ first;
+            const uint32_t u = j < n ? order_key(v[i]) ^ flip : first;
+            if (kLds && j < n) kc[j] = u;
+            if (so && j < n) so[j] = v[i];
+            diff |= u ^ first;
         }
     }
 #pragma unroll
@@ -377,13 +388,13 @@ __global__ __launch_bounds__(256) void pack_qsel_kernel(const T* __restrict__ q,
 // ----------------------------------------------------------------------------- launchers
 
 hipError_t launch_qstats(const SelShape& s, const void* q, const int64_t* prior_len, double* part, float* qcos,
-                         float* qrn, hipStream_t st) {
+                         float* qrn, uint32_t* zero, int64_t zero_n, hipStream_t st) {
     const int nblk = (s.C + kQRows - 1) / kQRows;
     dim3 grid(s.batch * s.h_q * nblk), block(256);
 #define KVSEL_QSTATS(T, D)                                                                                         \
     do {                                                                                                           \
         hipLaunchKernelGGL((qsum_kernel<T, D>), grid, block, 0, st, (const T*)q, s.h_q, s.C, nblk, prior_len,      \
-                           s.budget, part);                                                                        \
+                           s.budget, part, zero, zero_n);                                                          \
         hipLaunchKernelGGL((qcos_kernel<T, D>), grid, block, 0, st, (const T*)q, s.h_q, s.C, nblk, prior_len,      \
                            s.budget, part, qcos, qrn);                                                             \
     } while (0)
@@ -399,14 +410,15 @@ hipError_t launch_qstats(const SelShape& s, const void* q, const int64_t* prior_
 }
 
 hipError_t launch_topk(int problems, int heads_per_seq, const float* scores, int64_t score_stride,
+                       int nsplit, int64_t split_stride, float* s_out,
                        const int64_t* prior_len, int n_fixed, int64_t budget, int k, int32_t* out,
                        int64_t out_stride, int mode, int64_t max_n, hipStream_t st) {
     if (max_n <= kLdsKeys)
-        hipLaunchKernelGGL(topk_kernel<true>, dim3(problems), dim3(kTopkThreads), 0, st, scores, score_stride,
-                           heads_per_seq, prior_len, n_fixed, budget, k, out, out_stride, mode);
+        hipLaunchKernelGGL(topk_kernel<true>, dim3(problems), dim3(kTopkThreads), 0, st, scores, score_stride, nsplit,
+                           split_stride, s_out, heads_per_seq, prior_len, n_fixed, budget, k, out, out_stride, mode);
     else
-        hipLaunchKernelGGL(topk_kernel<false>, dim3(problems), dim3(kTopkThreads), 0, st, scores, score_stride,
-                           heads_per_seq, prior_len, n_fixed, budget, k, out, out_stride, mode);
+        hipLaunchKernelGGL(topk_kernel<false>, dim3(problems), dim3(kTopkThreads), 0, st, scores, score_stride, nsplit,
+                           split_stride, s_out, heads_per_seq, prior_len, n_fixed, budget, k, out, out_stride, mode);
     return hipGetLastError();
 }
 
