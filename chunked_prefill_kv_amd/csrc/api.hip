@@ -8,7 +8,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/kvsel.h"
+#include "kvsel.h"
 #include "launch.h"
 
 using namespace kvsel;

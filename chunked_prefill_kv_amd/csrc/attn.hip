@@ -40,8 +40,9 @@ __device__ __forceinline__ int sigma(int m) {
 
 // ----------------------------------------------------------------------------- bf16 MFMA kernel
 //
-// Workgroup: 4 waves x 32 query rows; rows are (token, head-in-group) pairs,
-// row = token * G + head, so a workgroup covers 128 / G tokens of all G heads.
+// Workgroup: WAVES waves x 32 query rows; rows are (token, head-in-group)
+// pairs, row = token * G + head, so a workgroup covers 32 * WAVES / G tokens of
+// all G heads, and every wave reads the same staged K/V tiles.
 // Per 64-key tile: S^T = K . Q^T (2 x KS MFMAs), online softmax on the lane's
 // query column, O^T += V^T . P^T (DB x 4 MFMAs).  K tiles are row-major
 // [key][d] and V tiles are [d][key] (written transposed by the pack kernel).
@@ -52,9 +53,15 @@ __device__ __forceinline__ int sigma(int m) {
 #define KVSEL_ATTN_PRIO 1
 #endif
 #define KVSEL_SETPRIO(p) do { if (KVSEL_ATTN_PRIO) __builtin_amdgcn_s_setprio(p); } while (0)
+#ifndef KVSEL_ATTN_WAVES
+#define KVSEL_ATTN_WAVES 4
+#endif
+#ifndef KVSEL_ATTN_PIPE
+#define KVSEL_ATTN_PIPE 0
+#endif
 
-template <int D, bool OUT_F32, int KT>
-__global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void attn_mfma_kernel(const uint16_t* __restrict__ q,
+template <int D, bool OUT_F32, int KT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ kall,
                                                            const uint16_t* __restrict__ vall,
                                                            const int32_t* __restrict__ nsel, int nk_pad, int C, int G,
@@ -65,8 +72,10 @@ __global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void attn_mfma_kernel(const 
     constexpr int NKB = KT / 32;            // 32-key MFMA blocks per tile
     constexpr int LDK = D + 8;
     constexpr int LDV = KT + 8;
-    constexpr int PK = KT * D / 8 / 256;    // 16-byte K pieces per thread per tile
-    constexpr int PV = D * KT / 8 / 256;    // 16-byte V^T pieces per thread per tile
+    constexpr int NT = 64 * WAVES;          // threads per workgroup
+    constexpr int ROWS = 32 * WAVES;        // query rows per workgroup
+    constexpr int PK = KT * D / 8 / NT;     // 16-byte K pieces per thread per tile
+    constexpr int PV = D * KT / 8 / NT;     // 16-byte V^T pieces per thread per tile
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT * LDK];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * LDV];
 
@@ -76,8 +85,8 @@ __global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void attn_mfma_kernel(const 
     const int b = bg / h_kv, g = bg % h_kv;
     const int nrows = G * C;
     const int n_s = nsel[b];
-    const int row_wg0 = rblk * 128;
-    const int wg_tmax = min(row_wg0 + 127, nrows - 1) / G;
+    const int row_wg0 = rblk * ROWS;
+    const int wg_tmax = min(row_wg0 + ROWS - 1, nrows - 1) / G;
     const int ntiles = (n_s + wg_tmax + 1 + KT - 1) / KT;
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
@@ -102,41 +111,42 @@ __global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void attn_mfma_kernel(const 
 
     const uint16_t* kb = kall + static_cast<int64_t>(bg) * nk_pad * D;
     const uint16_t* vb = vall + static_cast<int64_t>(bg) * D * nk_pad;
-    // Next-tile staging in two halves: K(t+1) is fetched at the start of tile t
-    // and written to LDS after t's S MFMAs, V(t+1) is fetched then and written
-    // at the end of t.  Buffer (t+1)&1 was last read in tile t-1, which every
-    // wave finished before the barrier that closed it, so both writes are safe.
-    u32x4 pst[PK > PV ? PK : PV];
+    // Staging with a full tile of latency for every load: V(t+1) is fetched at
+    // the start of tile t and written to LDS at its end; K(t+1), fetched in the
+    // middle of tile t-1, is written after t's S MFMAs and K(t+2) is fetched
+    // then.  Buffer (t+1)&1 was last read in tile t-1 and buffer t&1 (K(t+2))
+    // in tile t, each closed by a barrier before the write.
+    u32x4 rk[PK], rv[PV];
     auto fetch_k = [&](int t) {
 #pragma unroll
         for (int i = 0; i < PK; ++i) {
-            const int p = tid + 256 * i;
+            const int p = tid + NT * i;
             const int r = p / (D / 8), c = p % (D / 8);
-            pst[i] = *reinterpret_cast<const u32x4*>(kb + static_cast<int64_t>(t * KT + r) * D + c * 8);
+            rk[i] = *reinterpret_cast<const u32x4*>(kb + static_cast<int64_t>(t * KT + r) * D + c * 8);
         }
     };
     auto stash_k = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < PK; ++i) {
-            const int p = tid + 256 * i;
+            const int p = tid + NT * i;
             const int r = p / (D / 8), c = p % (D / 8);
-            *reinterpret_cast<u32x4*>(&k_lds[buf][r * LDK + c * 8]) = pst[i];
+            *reinterpret_cast<u32x4*>(&k_lds[buf][r * LDK + c * 8]) = rk[i];
         }
     };
     auto fetch_v = [&](int t) {
 #pragma unroll
         for (int i = 0; i < PV; ++i) {
-            const int p = tid + 256 * i;
+            const int p = tid + NT * i;
             const int d = p / (KT / 8), j = p % (KT / 8);
-            pst[i] = *reinterpret_cast<const u32x4*>(vb + static_cast<int64_t>(d) * nk_pad + t * KT + j * 8);
+            rv[i] = *reinterpret_cast<const u32x4*>(vb + static_cast<int64_t>(d) * nk_pad + t * KT + j * 8);
         }
     };
     auto stash_v = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < PV; ++i) {
-            const int p = tid + 256 * i;
+            const int p = tid + NT * i;
             const int d = p / (KT / 8), j = p % (KT / 8);
-            *reinterpret_cast<u32x4*>(&v_lds[buf][d * LDV + j * 8]) = pst[i];
+            *reinterpret_cast<u32x4*>(&v_lds[buf][d * LDV + j * 8]) = rv[i];
         }
     };
 
@@ -226,29 +236,113 @@ __global__ __launch_bounds__(256, KT == 32 ? 3 : 2) void attn_mfma_kernel(const 
         }
     };
 
+    // Variant: one max/rescale per tile, then a branch-free region in which the
+    // P.V MFMAs of block kb interleave with the exponentials of block kb+1.
+    auto tile_pipe = [&](const int buf, const int s0, auto mask_tag, auto&& mid) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        f32x16 sacc[NKB];
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2) {
+            sacc[kb2] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[buf][(32 * kb2 + krow) * LDK + 16 * ks + 8 * half]);
+                sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb2], 0, 0, 0);
+            }
+        }
+        mid();
+        if (MASK) {
+#pragma unroll
+            for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int sl = s0 + 32 * kb2 + 16 * (r >> 3) + 8 * half + (r & 7);
+                    if (sl > lim) sacc[kb2][r] = -INFINITY;
+                }
+        }
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb2][r]);
+        mt = half_max(mt);
+        const float m_new = fmaxf(m, mt);
+        if (__ballot((m_new - m) * cl2 > 8.0f) != 0ull) {
+            const float alpha = __builtin_amdgcn_exp2f((m - m_new) * cl2);
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            m = m_new;
+        }
+        const float mc = m * cl2;
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2) {
+            bf16x8 vf[DB][2];
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int k16 = 0; k16 < 2; ++k16)
+                    vf[db][k16] = *reinterpret_cast<const bf16x8*>(&v_lds[buf][(32 * db + col) * LDV + 32 * kb2 + 16 * k16 + 8 * half]);
+            bf16x8 pf[2];
+#pragma unroll
+            for (int k16 = 0; k16 < 2; ++k16) {
+                u32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e], cl2, -mc));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e + 1], cl2, -mc));
+                    l += p0 + p1;
+                    w[e] = pack_bf16x2(p0, p1);
+                }
+                pf[k16] = __builtin_bit_cast(bf16x8, w);
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int k16 = 0; k16 < 2; ++k16)
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][k16], pf[k16], o[db], 0, 0, 0);
+        }
+        // scheduling of the branch-free region: V reads, block 0's exponentials,
+        // then block 0's P.V MFMAs interleaved with block 1's exponentials
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 40, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    };
+
     fetch_k(0);
-    stash_k(0);
     fetch_v(0);
+    stash_k(0);
     stash_v(0);
+    if (ntiles > 1) fetch_k(1);
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
-        const bool more = t + 1 < ntiles;
-        if (more) fetch_k(t + 1);
+        if (t + 1 < ntiles) fetch_v(t + 1);
         auto mid = [&] {
-            if (more) {
-                stash_k(buf ^ 1);
-                fetch_v(t + 1);
-            }
+            if (t + 1 < ntiles) stash_k(buf ^ 1);
+            if (t + 2 < ntiles) fetch_k(t + 2);
         };
         const int s0 = t * KT;
         if (wave_active && s0 <= n_s + w_tmax) {
-            if (s0 + KT > n_s + w_tmin + 1) tile(buf, s0, std::true_type{}, mid);
-            else tile(buf, s0, std::false_type{}, mid);
+            if (KVSEL_ATTN_PIPE) {
+                if (s0 + KT > n_s + w_tmin + 1) tile_pipe(buf, s0, std::true_type{}, mid);
+                else tile_pipe(buf, s0, std::false_type{}, mid);
+            } else {
+                if (s0 + KT > n_s + w_tmin + 1) tile(buf, s0, std::true_type{}, mid);
+                else tile(buf, s0, std::false_type{}, mid);
+            }
         } else {
             mid();
         }
-        if (more) stash_v(buf ^ 1);
+        if (t + 1 < ntiles) stash_v(buf ^ 1);
         __syncthreads();
     }
 
@@ -350,19 +444,28 @@ __global__ __launch_bounds__(128) void attn_valu_kernel(const float* __restrict_
 
 hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const void* vall, const int32_t* nsel,
                        int nk_pad, float scale, void* out, bool out_f32, hipStream_t st) {
-    const int row_blocks = (s.G * s.C + 127) / 128;
-    dim3 grid(s.batch * s.h_kv * row_blocks);
+    const int bgs = s.batch * s.h_kv;
     if (s.esz == 2) {
+        // 8-wave workgroups share one staged copy of every K/V tile; fall back to
+        // 4 waves when that would leave fewer than 256 workgroups
+        const int rb8 = (s.G * s.C + 255) / 256, rb4 = (s.G * s.C + 127) / 128;
+        const bool w8 = KVSEL_ATTN_WAVES == 8 && bgs * rb8 >= 256;
+        const int row_blocks = w8 ? rb8 : rb4;
+        dim3 grid(bgs * row_blocks), block(w8 ? 512 : 256);
         const float cl2 = scale * 1.4426950408889634f;
         const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)kall, *vv = (const uint16_t*)vall;
+#define KVSEL_ATTN(D, F32, W) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, KVSEL_ATTN_KT, W>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out)
         if (s.d == 128) {
-            if (out_f32) hipLaunchKernelGGL((attn_mfma_kernel<128, true, KVSEL_ATTN_KT>), grid, dim3(256), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out);
-            else hipLaunchKernelGGL((attn_mfma_kernel<128, false, KVSEL_ATTN_KT>), grid, dim3(256), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out);
+            if (w8) { if (out_f32) KVSEL_ATTN(128, true, 8); else KVSEL_ATTN(128, false, 8); }
+            else { if (out_f32) KVSEL_ATTN(128, true, 4); else KVSEL_ATTN(128, false, 4); }
         } else {
-            if (out_f32) hipLaunchKernelGGL((attn_mfma_kernel<64, true, KVSEL_ATTN_KT>), grid, dim3(256), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out);
-            else hipLaunchKernelGGL((attn_mfma_kernel<64, false, KVSEL_ATTN_KT>), grid, dim3(256), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out);
+            if (w8) { if (out_f32) KVSEL_ATTN(64, true, 8); else KVSEL_ATTN(64, false, 8); }
+            else { if (out_f32) KVSEL_ATTN(64, true, 4); else KVSEL_ATTN(64, false, 4); }
         }
+#undef KVSEL_ATTN
     } else {
+        const int row_blocks = (s.G * s.C + 127) / 128;
+        dim3 grid(bgs * row_blocks);
         const float *qq = (const float*)q, *kk = (const float*)kall, *vv = (const float*)vall;
         if (s.d == 128) {
             if (out_f32) hipLaunchKernelGGL((attn_valu_kernel<128, true>), grid, dim3(128), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, scale, out);
