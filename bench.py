@@ -34,6 +34,22 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
 
 
+def measured_traffic(kernel_src: str, summary: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when
+    the kernel source has changed since those counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(summary).read()
+        want = re.search(r"kernel_source_sha256_16: (\w+)", text).group(1)
+        have = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+        if want != have:
+            return None
+        return float(re.search(r"traffic_bytes_per_launch: (\d+)", text).group(1))
+    except (OSError, AttributeError):
+        return None
+
+
 def algorithmic_work(wl, starts, lens):
     """Per-chunk algorithmic work of the method (see the design notes):
     attention: 4*d FLOP per (query row, visible key) pair, H_q*(C*B_eff + C(C+1)/2) pairs;
@@ -148,7 +164,11 @@ def main():
     n_att, ms_att = tr["attn"]
     att_tflops = sum(att_flop) * args.steps / (ms_att * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(att_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(att_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(att_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(os.path.join(ROOT, "chunked_prefill_kv_amd", "csrc", "attn.hip"),
+                                            os.path.join(ROOT, "profiles", "attn_mfma_llama8b_32k_traffic.md"))
+                if wl.name == "llama8b_32k" else None,
+                "algorithmic_bytes_per_launch": sum(att_bytes) / len(att_bytes),
                 "kernel": "attn_mfma_kernel<128,bf16 out>",
                 "launches": n_att, "avg_launch_us": round(ms_att * 1e3 / n_att, 2),
                 "algorithmic_flop_per_launch": sum(att_flop) / len(att_flop)}
