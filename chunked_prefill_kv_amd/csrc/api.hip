@@ -176,7 +176,7 @@ SelShape make_shape(const kvsel_heads* h, const kvsel_batch* b, const kvsel_para
 // ----------------------------------------------------------------------------- workspace layout
 
 struct Layout {
-    size_t qpart, qcos, qrn, keep, qsel, rq, scores, topb, idx, nsel, kall, vall, total;
+    size_t qpart, qcos, qrn, keep, qsel, rq, scores, topb, idx, nsel, kall, vall, apart, total;
     int nk_pad;
 };
 
@@ -200,6 +200,7 @@ Layout layout(const SelShape& s, bool with_attn) {
     if (with_attn) {
         L.kall = take(bg * L.nk_pad * s.d * s.esz);
         L.vall = take(bg * L.nk_pad * s.d * s.esz);
+        L.apart = take(attn_part_bytes(s));
     }
     L.total = off;
     return L;
@@ -304,7 +305,7 @@ kvsel_status kvsel_sparse_attn_workspace_size(const kvsel_heads* heads, const kv
     SelShape s = make_shape(heads, batch, nullptr, 0);
     const int nk_pad = static_cast<int>(round_up(int64_t(n_sel_max) + s.C, 64));
     const size_t kv = size_t(s.batch) * s.h_kv * nk_pad * s.d * s.esz;
-    *bytes = align256(size_t(s.batch) * 4) + 2 * align256(kv);
+    *bytes = align256(size_t(s.batch) * 4) + 2 * align256(kv) + align256(attn_part_bytes(s));
     return KVSEL_OK;
 }
 
@@ -354,6 +355,7 @@ kvsel_status kvsel_sparse_attn(const kvsel_heads* heads, const kvsel_batch* batc
     int32_t* nsel_ws = at<int32_t>(workspace, 0);
     void* kall = at<void>(workspace, align256(size_t(s.batch) * 4));
     void* vall = at<void>(workspace, align256(size_t(s.batch) * 4) + align256(kv));
+    float* apart = at<float>(workspace, align256(size_t(s.batch) * 4) + 2 * align256(kv));
     PackSrc src{};
     src.k_compact = k_sel;
     src.v_compact = v_sel;
@@ -362,7 +364,7 @@ kvsel_status kvsel_sparse_attn(const kvsel_heads* heads, const kvsel_batch* batc
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const float scale = heads->scale > 0.0f ? heads->scale : 1.0f / std::sqrt(static_cast<float>(heads->d));
     KVSEL_TRY(traced(KVSEL_K_PACK, hs, [&] { return launch_pack(s, src, k_chunk, v_chunk, nk_pad, kall, vall, nsel_ws, hs); }), "pack");
-    KVSEL_TRY(traced(KVSEL_K_ATTN, hs, [&] { return launch_attn(s, q, kall, vall, nsel_ws, nk_pad, scale, out, out_dtype == KVSEL_F32, hs); }), "attention");
+    KVSEL_TRY(traced(KVSEL_K_ATTN, hs, [&] { return launch_attn(s, q, kall, vall, nsel_ws, nk_pad, scale, out, out_dtype == KVSEL_F32, apart, hs); }), "attention");
     return KVSEL_OK;
 }
 
@@ -399,7 +401,7 @@ kvsel_status kvsel_prefill_chunk(const kvsel_heads* heads, const kvsel_batch* ba
     KVSEL_TRY(traced(KVSEL_K_PACK, hs, [&] { return launch_pack(s, src, k_chunk, v_chunk, L.nk_pad, at<void>(workspace, L.kall), at<void>(workspace, L.vall),
                           nsel, hs); }), "pack");
     KVSEL_TRY(traced(KVSEL_K_ATTN, hs, [&] { return launch_attn(s, q, at<void>(workspace, L.kall), at<void>(workspace, L.vall), nsel, L.nk_pad, scale, out,
-                          out_dtype == KVSEL_F32, hs); }), "attention");
+                          out_dtype == KVSEL_F32, at<float>(workspace, L.apart), hs); }), "attention");
     // the cache append happens inside the pack kernel (it reads the chunk's rows anyway)
     return KVSEL_OK;
 }

@@ -66,7 +66,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
                                                            const uint16_t* __restrict__ vall,
                                                            const int32_t* __restrict__ nsel, int nk_pad, int C, int G,
                                                            int h_kv, int row_blocks, float cl2,
-                                                           void* __restrict__ out) {
+                                                           void* __restrict__ out, int ksplit,
+                                                           float* __restrict__ part) {
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
     constexpr int NKB = KT / 32;            // 32-key MFMA blocks per tile
@@ -79,15 +80,23 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT * LDK];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * LDV];
 
+    // slot -> (KV head, row block, key split); later row blocks (more keys) first
     const int slot = xcd_slot(blockIdx.x, gridDim.x);
-    const int bg = slot / row_blocks;
-    const int rblk = row_blocks - 1 - slot % row_blocks;      // later tokens (more keys) first
+    const int bg = slot / (row_blocks * ksplit);
+    const int rem = slot % (row_blocks * ksplit);
+    const int rblk = row_blocks - 1 - rem / ksplit;
+    const int ksp = rem % ksplit;
     const int b = bg / h_kv, g = bg % h_kv;
     const int nrows = G * C;
     const int n_s = nsel[b];
     const int row_wg0 = rblk * ROWS;
     const int wg_tmax = min(row_wg0 + ROWS - 1, nrows - 1) / G;
-    const int ntiles = (n_s + wg_tmax + 1 + KT - 1) / KT;
+    const int ntiles_all = (n_s + wg_tmax + 1 + KT - 1) / KT;
+    // with ksplit > 1 this workgroup takes tiles [t_beg, t_end) and leaves an
+    // unnormalised partial (O, running max, row sum) for the merge kernel
+    const int per = (ntiles_all + ksplit - 1) / ksplit;
+    const int t_beg = min(ntiles_all, ksp * per);
+    const int ntiles = min(ntiles_all, t_beg + per) - t_beg;
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const int half = lane >> 5, col = lane & 31;
@@ -203,7 +212,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
             mt = half_max(mt);
             const float m_new = fmaxf(m, mt);
             if (__ballot((m_new - m) * cl2 > 8.0f) != 0ull) {
-                const float alpha = __builtin_amdgcn_exp2f((m - m_new) * cl2);
+                const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m - m_new) * cl2);
                 l *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
@@ -211,7 +220,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
                     for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
                 m = m_new;
             }
-            const float mc = m * cl2;
+            const float mc = m == -INFINITY ? 0.0f : m * cl2;   // no visible key yet: every p is 0
             bf16x8 pf[2];
             KVSEL_SETPRIO(0);
 #pragma unroll
@@ -268,7 +277,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
         mt = half_max(mt);
         const float m_new = fmaxf(m, mt);
         if (__ballot((m_new - m) * cl2 > 8.0f) != 0ull) {
-            const float alpha = __builtin_amdgcn_exp2f((m - m_new) * cl2);
+            const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m - m_new) * cl2);
             l *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
@@ -276,7 +285,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
                 for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
             m = m_new;
         }
-        const float mc = m * cl2;
+        const float mc = m == -INFINITY ? 0.0f : m * cl2;   // no visible key yet: every p is 0
 #pragma unroll
         for (int kb2 = 0; kb2 < NKB; ++kb2) {
             bf16x8 vf[DB][2];
@@ -317,18 +326,21 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     };
 
-    fetch_k(0);
-    fetch_v(0);
-    stash_k(0);
-    stash_v(0);
-    if (ntiles > 1) fetch_k(1);
+    if (ntiles > 0) {
+        fetch_k(t_beg);
+        fetch_v(t_beg);
+        stash_k(0);
+        stash_v(0);
+        if (ntiles > 1) fetch_k(t_beg + 1);
+    }
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < ntiles) fetch_v(t + 1);
+    for (int u = 0; u < ntiles; ++u) {           // u: tile within this workgroup's range
+        const int t = t_beg + u;
+        const int buf = u & 1;
+        if (u + 1 < ntiles) fetch_v(t + 1);
         auto mid = [&] {
-            if (t + 1 < ntiles) stash_k(buf ^ 1);
-            if (t + 2 < ntiles) fetch_k(t + 2);
+            if (u + 1 < ntiles) stash_k(buf ^ 1);
+            if (u + 2 < ntiles) fetch_k(t + 2);
         };
         const int s0 = t * KT;
         if (wave_active && s0 <= n_s + w_tmax) {
@@ -342,12 +354,30 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
         } else {
             mid();
         }
-        if (t + 1 < ntiles) stash_v(buf ^ 1);
+        if (u + 1 < ntiles) stash_v(buf ^ 1);
         __syncthreads();
     }
 
     l = half_sum(l);
     if (!rvalid) return;
+    if (ksplit > 1) {                            // partial: O unnormalised, (m, l) per row
+        const int64_t rows_total = static_cast<int64_t>(gridDim.x / (row_blocks * ksplit)) * nrows;
+        float* po = part + static_cast<int64_t>(ksp) * rows_total * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int d0 = 32 * db + 8 * a4 + 4 * half;
+                *reinterpret_cast<f32x4*>(po + qoff + d0) =
+                    f32x4{o[db][4 * a4 + 0], o[db][4 * a4 + 1], o[db][4 * a4 + 2], o[db][4 * a4 + 3]};
+            }
+        if (half == 0) {
+            float* pml = part + static_cast<int64_t>(ksplit) * rows_total * D + (static_cast<int64_t>(ksp) * rows_total + qoff / D) * 2;
+            pml[0] = m;
+            pml[1] = l;
+        }
+        return;
+    }
     const float inv = 1.0f / l;
     // O^T tile: register r of block db holds d = 32*db + 8*(r>>2) + 4*half + (r&3)
 #pragma unroll
@@ -365,6 +395,39 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
                 dst[1] = pack_bf16x2(v2, v3);
             }
         }
+}
+
+// ----------------------------------------------------------------------------- split merge
+//
+// out = sum_s w_s O_s / sum_s w_s l_s with w_s = exp2((m_s - max_s m_s) * cl2):
+// the key-split partials of one row combined as one softmax over all its keys.
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part, int64_t rows, int ksplit,
+                                                         float cl2, void* __restrict__ out) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (row, 4-column group)
+    if (i >= rows * (D / 4)) return;
+    const int64_t row = i / (D / 4);
+    const int c4 = static_cast<int>(i % (D / 4));
+    const float* pml = part + static_cast<int64_t>(ksplit) * rows * D;
+    float mx = -INFINITY;
+    for (int s = 0; s < ksplit; ++s) mx = fmaxf(mx, pml[(s * rows + row) * 2]);
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float den = 0.0f;
+    for (int s = 0; s < ksplit; ++s) {
+        const float ms = pml[(s * rows + row) * 2], ls = pml[(s * rows + row) * 2 + 1];
+        const float w = ls > 0.0f ? __builtin_amdgcn_exp2f((ms - mx) * cl2) : 0.0f;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(part + (s * rows + row) * D + 4 * c4);
+        acc += w * v;
+        den += w * ls;
+    }
+    const float inv = 1.0f / den;
+    if (OUT_F32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + row * D + 4 * c4) = acc * inv;
+    } else {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + row * D + 4 * c4);
+        dst[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+        dst[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    }
 }
 
 // ----------------------------------------------------------------------------- fp32 VALU kernel
@@ -442,8 +505,23 @@ __global__ __launch_bounds__(128) void attn_valu_kernel(const float* __restrict_
 
 // ----------------------------------------------------------------------------- launcher
 
+int attn_ksplit(const SelShape& s) {
+    if (s.esz != 2) return 1;
+    const int64_t wgs = int64_t(s.batch) * s.h_kv * ((s.G * s.C + 127) / 128);
+    int k = 1;
+    while (k < 4 && wgs * k < 512) k *= 2;            // at least two workgroups per CU
+    return k;
+}
+
+size_t attn_part_bytes(const SelShape& s) {
+    const int k = attn_ksplit(s);
+    if (k == 1) return 0;
+    const size_t rows = size_t(s.batch) * s.h_q * s.C;
+    return size_t(k) * rows * (s.d + 2) * 4;
+}
+
 hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const void* vall, const int32_t* nsel,
-                       int nk_pad, float scale, void* out, bool out_f32, hipStream_t st) {
+                       int nk_pad, float scale, void* out, bool out_f32, float* part, hipStream_t st) {
     const int bgs = s.batch * s.h_kv;
     if (s.esz == 2) {
         // 8-wave workgroups share one staged copy of every K/V tile; fall back to
@@ -451,10 +529,11 @@ hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const
         const int rb8 = (s.G * s.C + 255) / 256, rb4 = (s.G * s.C + 127) / 128;
         const bool w8 = KVSEL_ATTN_WAVES == 8 && bgs * rb8 >= 256;
         const int row_blocks = w8 ? rb8 : rb4;
-        dim3 grid(bgs * row_blocks), block(w8 ? 512 : 256);
+        const int ksplit = w8 ? 1 : attn_ksplit(s);
+        dim3 grid(bgs * row_blocks * ksplit), block(w8 ? 512 : 256);
         const float cl2 = scale * 1.4426950408889634f;
         const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)kall, *vv = (const uint16_t*)vall;
-#define KVSEL_ATTN(D, F32, W) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, KVSEL_ATTN_KT, W>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out)
+#define KVSEL_ATTN(D, F32, W) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, KVSEL_ATTN_KT, W>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part)
         if (s.d == 128) {
             if (w8) { if (out_f32) KVSEL_ATTN(128, true, 8); else KVSEL_ATTN(128, false, 8); }
             else { if (out_f32) KVSEL_ATTN(128, true, 4); else KVSEL_ATTN(128, false, 4); }
@@ -463,6 +542,17 @@ hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const
             else { if (out_f32) KVSEL_ATTN(64, true, 4); else KVSEL_ATTN(64, false, 4); }
         }
 #undef KVSEL_ATTN
+        if (ksplit > 1) {
+            const int64_t rows = int64_t(s.batch) * s.h_q * s.C;
+            const dim3 mg(static_cast<unsigned>((rows * (s.d / 4) + 255) / 256));
+            if (s.d == 128) {
+                if (out_f32) hipLaunchKernelGGL((attn_merge_kernel<128, true>), mg, dim3(256), 0, st, part, rows, ksplit, cl2, out);
+                else hipLaunchKernelGGL((attn_merge_kernel<128, false>), mg, dim3(256), 0, st, part, rows, ksplit, cl2, out);
+            } else {
+                if (out_f32) hipLaunchKernelGGL((attn_merge_kernel<64, true>), mg, dim3(256), 0, st, part, rows, ksplit, cl2, out);
+                else hipLaunchKernelGGL((attn_merge_kernel<64, false>), mg, dim3(256), 0, st, part, rows, ksplit, cl2, out);
+            }
+        }
     } else {
         const int row_blocks = (s.G * s.C + 127) / 128;
         dim3 grid(bgs * row_blocks);

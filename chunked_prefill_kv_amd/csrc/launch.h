@@ -106,9 +106,14 @@ struct PackSrc {
 hipError_t launch_pack(const SelShape& s, const PackSrc& src, const void* k_chunk, const void* v_chunk,
                        int nk_pad, void* kall, void* vall, int32_t* nsel_out, hipStream_t st);
 
-// Step 5 over the packed layout; out is fp32 (out_f32) or bf16.
+// Step 5 over the packed layout; out is fp32 (out_f32) or bf16.  When the
+// grid would hold fewer than two workgroups per CU the key tiles of every row
+// block are split over attn_ksplit(s) workgroups whose partials (fp32 scratch
+// `part` of attn_part_bytes(s) bytes) a merge kernel combines.
+int attn_ksplit(const SelShape& s);
+size_t attn_part_bytes(const SelShape& s);
 hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const void* vall,
                        const int32_t* nsel, int nk_pad, float scale, void* out, bool out_f32,
-                       hipStream_t st);
+                       float* part, hipStream_t st);
 
 }  // namespace kvsel
