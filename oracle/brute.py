@@ -34,10 +34,21 @@ def keep_for_head(rows: List[List[float]], n_q: int) -> List[int]:
     return sorted(i for _, i in ranked[:n_q])
 
 
+def _unit(a: Sequence[float]) -> List[float]:
+    n = math.sqrt(_dot(a, a))
+    return [0.0 if n == 0.0 else x / n for x in a]
+
+
 def chunk_step(Q: List[List[List[float]]], Kc: List[List[List[float]]], Vc: List[List[List[float]]],
                Kp: List[List[List[float]]], Vp: List[List[List[float]]], n_q: int, B: int,
-               scale: float | None = None) -> dict:
-    """Q[h][i][e]; Kc/Vc[g][t][e] (chunk); Kp/Vp[g][j][e] (prior cache, T rows)."""
+               scale: float | None = None, pooling: str = "head") -> dict:
+    """Q[h][i][e]; Kc/Vc[g][t][e] (chunk); Kp/Vp[g][j][e] (prior cache, T rows).
+
+    pooling="head": S = mean over the group's heads of the max over each head's
+    kept queries of the cosine.  pooling="group" (QuoKA article, Table 4
+    caption: cost in KV heads): the group's unit query rows are averaged per
+    token first, the query rule picks tokens of that pooled stream, and S =
+    max over kept tokens of (pooled row . key) / |key|."""
     H_q, C, d = len(Q), len(Q[0]), len(Q[0][0])
     H_kv, T = len(Kp), len(Kp[0])
     G = H_q // H_kv
@@ -45,7 +56,22 @@ def chunk_step(Q: List[List[List[float]]], Kc: List[List[List[float]]], Vc: List
         scale = 1.0 / math.sqrt(d)
     keep = None
     S = None
-    if T > B:
+    if T > B and pooling == "group":
+        pooled = []
+        for g in range(H_kv):
+            rows = []
+            for i in range(C):
+                units = [_unit(Q[h][i]) for h in range(g * G, (g + 1) * G)]
+                rows.append([sum(u[e] for u in units) / G for e in range(d)])
+            pooled.append(rows)
+        keep = [keep_for_head(pooled[g], n_q) for g in range(H_kv)]
+        S = [[0.0] * T for _ in range(H_kv)]
+        for g in range(H_kv):
+            for j in range(T):
+                kn = math.sqrt(_dot(Kp[g][j], Kp[g][j]))
+                best = max(_dot(pooled[g][i], Kp[g][j]) for i in keep[g])
+                S[g][j] = 0.0 if kn == 0.0 else best / kn
+    elif T > B:
         keep = [keep_for_head(Q[h], n_q) for h in range(H_q)]
         S = [[0.0] * T for _ in range(H_kv)]
         for g in range(H_kv):
@@ -54,6 +80,7 @@ def chunk_step(Q: List[List[List[float]]], Kc: List[List[List[float]]], Vc: List
                 for h in range(g * G, (g + 1) * G):
                     tot += max(_cos(Q[h][i], Kp[g][j]) for i in keep[h])
                 S[g][j] = tot / G
+    if T > B:
         idx = []
         for g in range(H_kv):
             ranked = sorted((-S[g][j], j) for j in range(T))
@@ -75,7 +102,7 @@ def chunk_step(Q: List[List[List[float]]], Kc: List[List[List[float]]], Vc: List
     return {"keep": keep, "S": S, "idx": idx, "O": O}
 
 
-def prefill(chunks, n_q: int, B: int, scale: float | None = None) -> List[dict]:
+def prefill(chunks, n_q: int, B: int, scale: float | None = None, pooling: str = "head") -> List[dict]:
     """chunks: list of (Q, Kc, Vc) nested lists; returns the per-chunk records."""
     Kp: List[List[List[float]]] = []
     Vp: List[List[List[float]]] = []
@@ -85,7 +112,7 @@ def prefill(chunks, n_q: int, B: int, scale: float | None = None) -> List[dict]:
         if not Kp:
             Kp = [[] for _ in range(H_kv)]
             Vp = [[] for _ in range(H_kv)]
-        out.append(chunk_step(Q, Kc, Vc, Kp, Vp, n_q, B, scale))
+        out.append(chunk_step(Q, Kc, Vc, Kp, Vp, n_q, B, scale, pooling))
         for g in range(H_kv):
             Kp[g] = Kp[g] + [list(r) for r in Kc[g]]
             Vp[g] = Vp[g] + [list(r) for r in Vc[g]]

@@ -42,6 +42,15 @@ Readings taken where the pages are silent (each is listed in the design notes):
 11. cos(x, y) = 0 when |x||y| = 0;
 12. top-B ties keep the lower key index; index sets are reported ascending.
 
+Group-pooled scoring (pooling="group", the other reading of the pooling order):
+the QuoKA article's Table 4 caption states the method's cost with the number
+of KV heads in place of the number of query heads.  Read as pooling first:
+for each KV head g and chunk token i, qbar[g, i] = the mean over the G query
+heads of g of q[h, i] / |q[h, i]| (a zero row contributes 0); the query
+sub-selection is the per-head rule applied to the pooled rows qbar[g]; the
+key score is S[g, j] = max over kept i of qbar[g, i] . k_j / |k_j|, which is
+the max over kept tokens of the mean over heads of cos(q[h, i], k_j).
+
 Every function takes fp64 arrays (exact widenings of the bf16 / fp32 inputs).
 Nothing here is pinned only to itself: see tests/test_oracle_pins.py.
 """
@@ -119,6 +128,36 @@ def key_scores(Qc: np.ndarray, keep: Sequence[np.ndarray], K: np.ndarray) -> np.
     return S
 
 
+# ----------------------------------------------------------------------------- group pooling
+
+def pooled_queries(Qc: np.ndarray, H_kv: int) -> np.ndarray:
+    """qbar[g, i] = (1/G) * sum over the G query heads h of KV head g of
+    q[h, i] / |q[h, i]| (0 for a zero row).  QuoKA article, Table 4 caption
+    (cost in KV heads) and the method paragraph (mean pooling over the group).
+    Qc: [H_q, C, d] -> [H_kv, C, d]."""
+    H_q, C, d = Qc.shape
+    G = H_q // H_kv
+    unit = _safe_div(Qc, _norms(Qc)[..., None])
+    return unit.reshape(H_kv, G, C, d).mean(axis=1)
+
+
+def key_scores_group(Qbar: np.ndarray, keep: Sequence[np.ndarray], K: np.ndarray) -> np.ndarray:
+    """S[g, j] = max over i in keep[g] of qbar[g, i] . k_j / |k_j| (0 for a zero key):
+    the max over the retained tokens of the mean over heads of the query-key
+    cosine.  QuoKA article, Fig. 1(b) (query-key cosine filter, max pooling over
+    queries) with the group's heads pooled first.
+    Qbar: [H_kv, C, d]; K: [H_kv, T, d] -> [H_kv, T]."""
+    H_kv, T, _ = K.shape
+    S = np.zeros((H_kv, T), dtype=np.float64)
+    for g in range(H_kv):
+        Qs = Qbar[g, np.asarray(keep[g], dtype=np.int64)]
+        kn = _norms(K[g])
+        for j0 in range(0, T, KEY_BLOCK):
+            j1 = min(T, j0 + KEY_BLOCK)
+            S[g, j0:j1] = _safe_div((Qs @ K[g, j0:j1].T).max(axis=0), kn[j0:j1])
+    return S
+
+
 # ----------------------------------------------------------------------------- step 4
 
 def top_b(S_g: np.ndarray, B: int) -> np.ndarray:
@@ -168,27 +207,35 @@ def attend(Qc: np.ndarray, K_sel: Sequence[np.ndarray], V_sel: Sequence[np.ndarr
 # ----------------------------------------------------------------------------- one chunk
 
 def select(Qc: np.ndarray, K_prior: np.ndarray, n_q: int, B: int,
-           keep: Optional[Sequence[np.ndarray]] = None) -> Dict[str, object]:
+           keep: Optional[Sequence[np.ndarray]] = None, pooling: str = "head") -> Dict[str, object]:
     """Steps 1-4 for one chunk against the prior cache K_prior [H_kv, T, d].
 
-    Returns keep (per query head), S [H_kv, T] (None when T <= B) and idx
-    (per KV head, ascending).  `keep` may be supplied to condition steps 2-4 on
-    a given query sub-selection.
+    Returns keep (per query head, or per KV head with pooling="group"), S
+    [H_kv, T] (None when T <= B) and idx (per KV head, ascending).  `keep` may
+    be supplied to condition steps 2-4 on a given query sub-selection.
     """
     H_kv, T, _ = K_prior.shape
     if T <= B:
         return {"keep": None, "S": None, "idx": [np.arange(T, dtype=np.int64) for _ in range(H_kv)]}
-    if keep is None:
-        keep = keep_all_heads(Qc, n_q)
-    S = key_scores(Qc, keep, K_prior)
+    if pooling == "group":
+        Qbar = pooled_queries(Qc, H_kv)
+        if keep is None:
+            keep = [query_keep(Qbar[g], n_q) for g in range(H_kv)]
+        S = key_scores_group(Qbar, keep, K_prior)
+    elif pooling == "head":
+        if keep is None:
+            keep = keep_all_heads(Qc, n_q)
+        S = key_scores(Qc, keep, K_prior)
+    else:
+        raise ValueError(f"unknown pooling {pooling!r}")
     return {"keep": list(keep), "S": S, "idx": [top_b(S[g], B) for g in range(H_kv)]}
 
 
 def prefill_chunk(Qc: np.ndarray, Kc: np.ndarray, Vc: np.ndarray,
                   K_prior: np.ndarray, V_prior: np.ndarray, n_q: int, B: int,
-                  scale: Optional[float] = None) -> Dict[str, object]:
+                  scale: Optional[float] = None, pooling: str = "head") -> Dict[str, object]:
     """Select over the prior cache, compact, attend (steps 1-6 of one chunk)."""
-    sel = select(Qc, K_prior, n_q, B)
+    sel = select(Qc, K_prior, n_q, B, pooling=pooling)
     idx = sel["idx"]
     K_sel = [K_prior[g, idx[g]] for g in range(K_prior.shape[0])]
     V_sel = [V_prior[g, idx[g]] for g in range(V_prior.shape[0])]
@@ -197,7 +244,7 @@ def prefill_chunk(Qc: np.ndarray, Kc: np.ndarray, Vc: np.ndarray,
 
 
 def prefill(chunks: Sequence[tuple], n_q: int, B: int, scale: Optional[float] = None,
-            keep_trace: bool = False) -> Dict[str, object]:
+            keep_trace: bool = False, pooling: str = "head") -> Dict[str, object]:
     """Whole-prompt chunked prefill: for chunk k (T = tokens so far) select over the
     cache, attend, then append the chunk's K/V (the cache grows by one chunk).
 
@@ -212,7 +259,7 @@ def prefill(chunks: Sequence[tuple], n_q: int, B: int, scale: Optional[float] = 
         H_kv, _, d = Kc.shape
         K_prior = np.concatenate(Ks, axis=1) if Ks else np.zeros((H_kv, 0, d))
         V_prior = np.concatenate(Vs, axis=1) if Vs else np.zeros((H_kv, 0, d))
-        r = prefill_chunk(Qc, Kc, Vc, K_prior, V_prior, n_q, B, scale)
+        r = prefill_chunk(Qc, Kc, Vc, K_prior, V_prior, n_q, B, scale, pooling)
         outs.append(r["O"])
         if keep_trace:
             trace.append(r)
