@@ -50,11 +50,13 @@ def measured_traffic(kernel_src: str, summary: str):
         return None
 
 
-def algorithmic_work(wl, starts, lens):
+def algorithmic_work(wl, starts, lens, pooling="head"):
     """Per-chunk algorithmic work of the method (see the design notes):
     attention: 4*d FLOP per (query row, visible key) pair, H_q*(C*B_eff + C(C+1)/2) pairs;
-    scan: 2*d FLOP per (kept query, prior key) pair, H_q*min(N_q,C)*T pairs, only when T > B;
+    scan: 2*d FLOP per (kept query, prior key) pair, H_q*min(N_q,C)*T pairs (H_kv*min(N_q,C)*T
+    pooled rows with the group-first order), only when T > B;
     scan bytes: the prior keys read once, H_kv*T*d*2."""
+    heads = wl.H_kv if pooling == "group" and wl.C > 1 else wl.H_q
     att_flop, scan_flop, scan_bytes, att_bytes = [], [], [], []
     for T, C in zip(starts, lens):
         beff = min(wl.B, T)
@@ -62,7 +64,7 @@ def algorithmic_work(wl, starts, lens):
         esz = 2 if wl.dtype == "bf16" else 4
         att_bytes.append(esz * wl.d * (2 * wl.H_q * C + 2 * wl.H_kv * (beff + C)))
         if T > wl.B:
-            scan_flop.append(2.0 * wl.d * wl.H_q * min(wl.n_q, C) * T)
+            scan_flop.append(2.0 * wl.d * heads * min(wl.n_q, C) * T)
             scan_bytes.append(esz * wl.H_kv * T * wl.d)
         else:
             scan_flop.append(0.0)
@@ -70,7 +72,7 @@ def algorithmic_work(wl, starts, lens):
     return att_flop, att_bytes, scan_flop, scan_bytes
 
 
-def cpu_baseline(wl, chunks, sample_every=8):
+def cpu_baseline(wl, chunks, sample_every=8, pooling="head"):
     """The oracle, as it stands, on every `sample_every`-th chunk (the last of each group)."""
     from chunked_prefill_kv_amd import gen
     from oracle import quoka
@@ -87,7 +89,7 @@ def cpu_baseline(wl, chunks, sample_every=8):
         Kp = np.concatenate([gen.to_f64(c[1]) for c in chunks[:k]], axis=1)
         Vp = np.concatenate([gen.to_f64(c[2]) for c in chunks[:k]], axis=1)
         t0 = time.perf_counter()
-        quoka.prefill_chunk(Qc, Kc, Vc, Kp, Vp, wl.n_q, wl.B)
+        quoka.prefill_chunk(Qc, Kc, Vc, Kp, Vp, wl.n_q, wl.B, pooling=pooling)
         t_total += time.perf_counter() - t0
         tokens += Qc.shape[1]
     return {"value": tokens / t_total, "unit": "tokens/s/layer", "cores": cores, "kind": "oracle",
@@ -103,6 +105,8 @@ def main():
     ap.add_argument("--workload", default="llama8b_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--lib", default=None, help="path of an alternative libkvsel.so build")
+    ap.add_argument("--pooling", choices=["head", "group"], default="head",
+                    help="order of the score poolings: per-head max then group mean (default), or group-pooled rows first")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (the reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -132,7 +136,8 @@ def main():
     wl = gen.WORKLOADS[args.workload]
     print(f"[bench] generating {wl.name} inputs", file=sys.stderr, flush=True)
     chunks = [gen.chunk_inputs(wl, k) for k in range(wl.n_chunks)]
-    r = runner.PromptRunner(wl, out_dtype=torch.bfloat16)
+    r = runner.PromptRunner(wl, out_dtype=torch.bfloat16,
+                            pooling=K.KVSEL_POOL_GROUP if args.pooling == "group" else K.KVSEL_POOL_HEAD)
     r.load(chunks)
     torch.cuda.synchronize()
 
@@ -160,7 +165,7 @@ def main():
     torch.cuda.synchronize()
     K.trace_stop()
     tr = K.trace_read()
-    att_flop, att_bytes, scan_flop, scan_bytes = algorithmic_work(wl, r.starts, r.lens)
+    att_flop, att_bytes, scan_flop, scan_bytes = algorithmic_work(wl, r.starts, r.lens, args.pooling)
     n_att, ms_att = tr["attn"]
     att_tflops = sum(att_flop) * args.steps / (ms_att * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(att_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -187,14 +192,14 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic (seeded shared-direction generator, sinks x4)",
         "config": {"workload": wl.name, "L": wl.L, "C": wl.C, "H_q": wl.H_q, "H_kv": wl.H_kv, "d": wl.d,
-                   "n_q": wl.n_q, "B": wl.B, "chunks": wl.n_chunks, "out": "bf16"},
+                   "n_q": wl.n_q, "B": wl.B, "chunks": wl.n_chunks, "out": "bf16", "pooling": args.pooling},
         "roofline": roofline,
         "kernels": kernels,
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, chunks)
+        out["cpu_baseline"] = cpu_baseline(wl, chunks, pooling=args.pooling)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvsel.so")
-SOURCES = ["api.hip", "select.hip", "topb.hip", "scan.hip", "copy.hip", "attn.hip"]
+SOURCES = ["api.hip", "select.hip", "pool.hip", "topb.hip", "scan.hip", "copy.hip", "attn.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -43,7 +44,7 @@ constexpr int64_t kMaxLen = int64_t(1) << 30;   // positions fit int32 kernel ar
 // ----------------------------------------------------------------------------- tracing
 
 const char* const kKernelNames[KVSEL_K_COUNT] = {"qstats", "qtopk", "qpack", "scan", "topb",
-                                                 "gather", "pack", "attn", "append"};
+                                                 "gather", "pack", "attn", "append", "qpool"};
 
 struct Trace {
     std::mutex mu;
@@ -116,6 +117,8 @@ kvsel_status check_params(const kvsel_params* p) {
     if (!p) return fail(KVSEL_ERR_INVALID_ARG, "params is NULL");
     if (p->n_q < 1) return fail(KVSEL_ERR_INVALID_ARG, "n_q=%d must be >= 1", p->n_q);
     if (p->budget < 1) return fail(KVSEL_ERR_INVALID_ARG, "budget=%d must be >= 1", p->budget);
+    if (p->pooling != KVSEL_POOL_HEAD && p->pooling != KVSEL_POOL_GROUP)
+        return fail(KVSEL_ERR_INVALID_ARG, "pooling=%d must be KVSEL_POOL_HEAD or KVSEL_POOL_GROUP", p->pooling);
     return KVSEL_OK;
 }
 
@@ -170,13 +173,29 @@ SelShape make_shape(const kvsel_heads* h, const kvsel_batch* b, const kvsel_para
     s.budget = p ? p->budget : 0;
     s.t_max = t_max;
     s.nsplit = (s.esz == 2 && s.nq_pad % 32 == 0) ? scan_splits(s.batch, s.h_kv, s.G, t_max) : 1;
+    // a single chunk token makes both pooling orders the same score: the
+    // group-pooled path is only taken for chunk_len > 1
+    s.pool = (p && p->pooling == KVSEL_POOL_GROUP && s.C > 1) ? 1 : 0;
+    s.qsplit = 0;
     return s;
+}
+
+// Scan shape of the group-pooled order: one pooled row stream per KV head
+// (G = 1), bf16 scans take the rows as [hi | lo] pairs on the MFMA path.
+SelShape pooled_shape(const SelShape& s) {
+    SelShape p = s;
+    p.h_q = s.h_kv;
+    p.G = 1;
+    p.nq_pad = s.esz == 4 ? s.nqp : static_cast<int>(round_up(s.nqp, 32));
+    p.nsplit = 1;
+    p.qsplit = s.esz == 2 ? 1 : 0;
+    return p;
 }
 
 // ----------------------------------------------------------------------------- workspace layout
 
 struct Layout {
-    size_t qpart, qcos, qrn, keep, qsel, rq, scores, topb, idx, nsel, kall, vall, apart, total;
+    size_t qpart, qcos, qrn, keep, qsel, rq, qbar, scores, topb, idx, nsel, kall, vall, apart, total;
     int nk_pad;
 };
 
@@ -189,8 +208,15 @@ Layout layout(const SelShape& s, bool with_attn) {
     L.qcos = take(bh * s.C * 4);
     L.qrn = take(bh * s.C * 4);
     L.keep = take(bh * s.nqp * 4);
-    L.qsel = take(bg * s.G * s.nq_pad * s.d * s.esz);
-    L.rq = take(bg * s.G * s.nq_pad * 4);
+    size_t qsel_bytes = bg * s.G * s.nq_pad * s.d * s.esz, rq_rows = bg * s.G * s.nq_pad;
+    if (s.pool) {                                   // pooled rows: 4*d bytes ([hi | lo] bf16 or fp32)
+        const SelShape p = pooled_shape(s);
+        qsel_bytes = std::max(qsel_bytes, bg * p.nq_pad * s.d * 4);
+        rq_rows = std::max(rq_rows, bg * p.nq_pad);
+    }
+    L.qsel = take(qsel_bytes);
+    L.rq = take(rq_rows * 4);
+    L.qbar = s.pool ? take(bg * s.C * s.d * 4) : 0;
     L.scores = take(bg * (s.t_max > 0 ? s.t_max : 1) * 4 * s.nsplit);
     L.topb = take(topb_scratch_bytes(static_cast<int>(bg), s.t_max, s.budget));
     L.idx = take(bg * s.budget * 4);
@@ -223,9 +249,23 @@ kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, 
     const int64_t* T = b->prior_len_dev;
     // the scan writes into the workspace (its split partials when s.nsplit > 1);
     // the top-B kernel adds the splits and stores the sum in `scores` if asked
-    float* S = (scores && s.nsplit == 1) ? scores : at<float>(ws, L.scores);
+    const SelShape sc = s.pool ? pooled_shape(s) : s;     // the scan's shape
+    float* S = (scores && sc.nsplit == 1) ? scores : at<float>(ws, L.scores);
     const int64_t split_stride = int64_t(s.batch) * s.h_kv * s.t_max;
-    if (any) {
+    if (any && s.pool) {
+        // group-pooled: the group's unit rows averaged per token, then steps
+        // 1-2 on the pooled rows as one head per KV head
+        int32_t* keep = q_keep ? q_keep : at<int32_t>(ws, L.keep);
+        float* qbar = at<float>(ws, L.qbar);
+        SelShape sq = sc;
+        sq.esz = 4;                                          // qbar is fp32
+        KVSEL_TRY(traced(KVSEL_K_QPOOL, st, [&] { return launch_qpool(s, q, T, qbar, st); }), "query pooling");
+        KVSEL_TRY(traced(KVSEL_K_QSTATS, st, [&] { return launch_qstats(sq, qbar, T, at<double>(ws, L.qpart), at<float>(ws, L.qcos), at<float>(ws, L.qrn), at<uint32_t>(ws, L.topb), int64_t(s.batch) * s.h_kv * 4096, st); }), "query statistics");
+        KVSEL_TRY(traced(KVSEL_K_QTOPK, st, [&] { return launch_topk(s.batch * s.h_kv, s.h_kv, at<float>(ws, L.qcos), s.C, 1, 0, nullptr, T, s.C, s.budget, s.nqp, keep, s.nqp,
+                              1, s.C, st); }), "query top-k");
+        KVSEL_TRY(traced(KVSEL_K_QPACK, st, [&] { return launch_pack_pooled(sc, qbar, keep, s.nqp, T, at<void>(ws, L.qsel), at<float>(ws, L.rq), st); }), "query packing");
+        KVSEL_TRY(traced(KVSEL_K_SCAN, st, [&] { return launch_scan(sc, at<void>(ws, L.qsel), at<float>(ws, L.rq), cv, T, S, s.t_max, st); }), "key scan");
+    } else if (any) {
         int32_t* keep = q_keep ? q_keep : at<int32_t>(ws, L.keep);
         KVSEL_TRY(traced(KVSEL_K_QSTATS, st, [&] { return launch_qstats(s, q, T, at<double>(ws, L.qpart), at<float>(ws, L.qcos), at<float>(ws, L.qrn), at<uint32_t>(ws, L.topb), int64_t(s.batch) * s.h_kv * 4096, st); }), "query statistics");
         KVSEL_TRY(traced(KVSEL_K_QTOPK, st, [&] { return launch_topk(s.batch * s.h_q, s.h_q, at<float>(ws, L.qcos), s.C, 1, 0, nullptr, T, s.C, s.budget, s.nqp, keep, s.nqp,
@@ -235,7 +275,7 @@ kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, 
         KVSEL_TRY(traced(KVSEL_K_SCAN, st, [&] { return launch_scan(s, at<void>(ws, L.qsel), at<float>(ws, L.rq), cv, T, S, s.t_max, st); }), "key scan");
     }
     float* comb = scores ? scores : S;
-    KVSEL_TRY(traced(KVSEL_K_TOPB, st, [&] { return launch_topb(s.batch * s.h_kv, s.h_kv, S, s.nsplit, split_stride, comb, s.t_max, T,
+    KVSEL_TRY(traced(KVSEL_K_TOPB, st, [&] { return launch_topb(s.batch * s.h_kv, s.h_kv, S, sc.nsplit, split_stride, comb, s.t_max, T,
                                                                 s.budget, s.t_max, any, at<uint32_t>(ws, L.topb), idx, st); }), "key top-B");
     return KVSEL_OK;
 }
@@ -281,7 +321,7 @@ kvsel_status kvsel_trace_read(int32_t* launches, float* total_ms, int32_t n) {
 
 const char* kvsel_kernel_name(int32_t id) { return (id >= 0 && id < KVSEL_K_COUNT) ? kKernelNames[id] : ""; }
 
-int32_t kvsel_version(void) { return 100; }
+int32_t kvsel_version(void) { return 101; }
 
 kvsel_status kvsel_workspace_size(const kvsel_heads* heads, const kvsel_batch* batch, const kvsel_params* params,
                                   size_t* bytes) {

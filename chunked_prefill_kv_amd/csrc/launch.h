@@ -17,6 +17,8 @@ struct SelShape {
     int64_t budget;
     int64_t t_max;                    // max_b T_b
     int nsplit;                       // MFMA scan: query-head groups per key tile (1 = no split)
+    int pool;                         // 0: per-head max then group mean; 1: group-pooled rows first
+    int qsplit;                       // MFMA scan rows are [hi | lo] bf16 pairs of fp32 rows (2*d elements)
 };
 
 // Choose how many query-head groups the MFMA scan splits a KV head into: a
@@ -70,6 +72,15 @@ hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int n
 hipError_t launch_pack_qsel(const SelShape& s, const void* q, const int32_t* keep, int64_t keep_stride,
                             const float* qrn, const int64_t* prior_len, void* qsel, float* rq,
                             hipStream_t st);
+
+// Group-pooled step 1 (s.pool == 1): qbar[b][g][i][d] fp32 = mean over the G
+// query heads of g of the unit query rows (sequences with T_b <= budget
+// skipped).
+hipError_t launch_qpool(const SelShape& s, const void* q, const int64_t* prior_len, float* qbar, hipStream_t st);
+// Q_sel of the pooled scan (sp: one "head" per KV head, G = 1): the kept qbar
+// rows, as [hi | lo] bf16 pairs when sp.qsplit, else fp32; rq = 1.
+hipError_t launch_pack_pooled(const SelShape& sp, const float* qbar, const int32_t* keep, int64_t keep_stride,
+                              const int64_t* prior_len, void* qsel, float* rq, hipStream_t st);
 
 // Step 2: S[b][g][j] for j < T_b (sequences with T_b > budget only).  With
 // s.nsplit > 1 the MFMA scan writes s.nsplit partial arrays, split k at

@@ -22,11 +22,15 @@ namespace kvsel {
 // 16 query rows of one key: the max over queries is in-register plus one
 // exchange between the two half-waves at the end of every head.
 //
+// With QK = 2 every Q_sel row is a pair [hi | lo] of bf16 rows whose sum is an
+// fp32 row (the group-pooled rows); both halves multiply the same key
+// fragments and accumulate into one fp32 product.
+//
 // The G query heads may be split over `nsplit` workgroups per key tile (more
 // workgroups when the cache or the KV head count is small); split s writes
 // the sum over its heads, scaled by 1/G, to S + s * split_stride and the top-B
 // kernel adds the splits in order.
-template <int D, int NB>
+template <int D, int NB, int QK>
 __global__ __launch_bounds__(256, 2) void scan_mfma_kernel(const uint16_t* __restrict__ qsel,
                                                            const float* __restrict__ rq, CacheView cv,
                                                            const int64_t* __restrict__ prior_len, int64_t budget,
@@ -34,10 +38,12 @@ __global__ __launch_bounds__(256, 2) void scan_mfma_kernel(const uint16_t* __res
                                                            float* __restrict__ S, int64_t s_stride,
                                                            int64_t split_stride) {
     constexpr int KS = D / 16;              // MFMA k-steps over the head dim
+    constexpr int KQ = D * QK;              // elements per Q_sel row ([hi | lo] pairs when QK = 2)
+    constexpr int KSQ = KQ / 16;            // k-steps per query row; key fragment ks % KS
     constexpr int KEYS = 4 * NB * 32;       // keys per workgroup
     constexpr int STAGE = 64;               // query rows per LDS stage
-    constexpr int LDQ = D + 8;              // padded LDS row (bf16 elements)
-    constexpr int PIECES = STAGE * D / 8;   // 16-byte pieces per stage
+    constexpr int LDQ = KQ + 8;             // padded LDS row (bf16 elements)
+    constexpr int PIECES = STAGE * KQ / 8;  // 16-byte pieces per stage
     constexpr int PPT = PIECES / 256;       // pieces per thread
     __shared__ __attribute__((aligned(16))) uint16_t qs[2][STAGE * LDQ];
     __shared__ __attribute__((aligned(16))) float rqs[2][STAGE];
@@ -82,7 +88,7 @@ __global__ __launch_bounds__(256, 2) void scan_mfma_kernel(const uint16_t* __res
 
     const int R = G / nsplit * nq_pad;                  // this split's query rows
     const int nstage = (R + STAGE - 1) / STAGE;
-    const uint16_t* qb = qsel + (static_cast<int64_t>(bg) * G * nq_pad + static_cast<int64_t>(split) * R) * D;
+    const uint16_t* qb = qsel + (static_cast<int64_t>(bg) * G * nq_pad + static_cast<int64_t>(split) * R) * KQ;
     const float* rqb = rq + static_cast<int64_t>(bg) * G * nq_pad + static_cast<int64_t>(split) * R;
 
     u32x4 pre[PPT];
@@ -91,9 +97,9 @@ __global__ __launch_bounds__(256, 2) void scan_mfma_kernel(const uint16_t* __res
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
             const int p = tid + 256 * i;
-            const int r = p / (D / 8), c8 = p % (D / 8);
+            const int r = p / (KQ / 8), c8 = p % (KQ / 8);
             const int row = s * STAGE + r;
-            pre[i] = row < R ? *reinterpret_cast<const u32x4*>(qb + static_cast<int64_t>(row) * D + c8 * 8)
+            pre[i] = row < R ? *reinterpret_cast<const u32x4*>(qb + static_cast<int64_t>(row) * KQ + c8 * 8)
                              : u32x4{0u, 0u, 0u, 0u};
         }
         if (tid < STAGE) {
@@ -105,7 +111,7 @@ __global__ __launch_bounds__(256, 2) void scan_mfma_kernel(const uint16_t* __res
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
             const int p = tid + 256 * i;
-            const int r = p / (D / 8), c8 = p % (D / 8);
+            const int r = p / (KQ / 8), c8 = p % (KQ / 8);
             *reinterpret_cast<u32x4*>(&qs[buf][r * LDQ + c8 * 8]) = pre[i];
         }
         if (tid < STAGE) rqs[buf][tid] = prq;
@@ -125,9 +131,9 @@ __global__ __launch_bounds__(256, 2) void scan_mfma_kernel(const uint16_t* __res
         for (int rb = 0; rb < STAGE / 32; ++rb) {
             const int row0 = s * STAGE + rb * 32;
             if (row0 < R) {
-                bf16x8 a[KS];
+                bf16x8 a[KSQ];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
+                for (int ks = 0; ks < KSQ; ++ks)
                     a[ks] = *reinterpret_cast<const bf16x8*>(&qs[buf][(rb * 32 + col) * LDQ + 16 * ks + 8 * half]);
                 float rv[16];
 #pragma unroll
@@ -139,8 +145,8 @@ __global__ __launch_bounds__(256, 2) void scan_mfma_kernel(const uint16_t* __res
                 for (int kb = 0; kb < NB; ++kb) {
                     f32x16 acc = {};
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], kf[kb][ks], acc, 0, 0, 0);
+                    for (int ks = 0; ks < KSQ; ++ks)
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], kf[kb][ks % KS], acc, 0, 0, 0);
                     float m = run[kb];
 #pragma unroll
                     for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[r] * rv[r]);
@@ -306,7 +312,7 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const E* __restrict__ qs
 hipError_t launch_scan(const SelShape& s, const void* qsel, const float* rq, const CacheView& cv,
                        const int64_t* prior_len, float* S, int64_t s_stride, hipStream_t st) {
     const int bgs = s.batch * s.h_kv;
-    if (s.esz == 2 && s.nq_pad == 1) {          // one query per head, G <= 16
+    if (s.esz == 2 && s.nq_pad == 1 && !s.qsplit) {   // one query per head, G <= 16
         const int tiles = static_cast<int>((s.t_max + 255) / 256);
         dim3 grid(bgs * tiles), block(256);
         if (s.d == 128) hipLaunchKernelGGL((scan_rows16_kernel<128>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride);
@@ -316,8 +322,13 @@ hipError_t launch_scan(const SelShape& s, const void* qsel, const float* rq, con
         const int tiles = static_cast<int>((s.t_max + 4 * NB * 32 - 1) / (4 * NB * 32));
         dim3 grid(bgs * tiles * s.nsplit), block(256);
         const int64_t split_stride = int64_t(bgs) * s_stride;
-        if (s.d == 128) hipLaunchKernelGGL((scan_mfma_kernel<128, NB>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, s.nsplit, S, s_stride, split_stride);
-        else hipLaunchKernelGGL((scan_mfma_kernel<64, NB>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, s.nsplit, S, s_stride, split_stride);
+#define KVSEL_SCAN(D, QK) hipLaunchKernelGGL((scan_mfma_kernel<D, NB, QK>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, s.nsplit, S, s_stride, split_stride)
+        if (s.qsplit) {
+            if (s.d == 128) KVSEL_SCAN(128, 2); else KVSEL_SCAN(64, 2);
+        } else {
+            if (s.d == 128) KVSEL_SCAN(128, 1); else KVSEL_SCAN(64, 1);
+        }
+#undef KVSEL_SCAN
     } else {
         const int tiles = static_cast<int>((s.t_max + 255) / 256);
         dim3 grid(bgs * tiles), block(256);

@@ -18,13 +18,14 @@ LIB_PATH = os.path.join(_PKG, "libkvsel.so")
 
 KVSEL_OK, KVSEL_ERR_INVALID_ARG, KVSEL_ERR_UNSUPPORTED, KVSEL_ERR_WORKSPACE, KVSEL_ERR_HIP = range(5)
 KVSEL_F32, KVSEL_BF16 = 0, 1
+KVSEL_POOL_HEAD, KVSEL_POOL_GROUP = 0, 1
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP"}
 
 # the exported symbols of include/kvsel.h
 EXPORTS = ("kvsel_workspace_size", "kvsel_sparse_attn_workspace_size", "kvsel_select", "kvsel_sparse_attn",
            "kvsel_prefill_chunk", "kvsel_last_error", "kvsel_version", "kvsel_trace_start", "kvsel_trace_stop",
            "kvsel_trace_read", "kvsel_kernel_name")
-KERNELS = ("qstats", "qtopk", "qpack", "scan", "topb", "gather", "pack", "attn", "append")
+KERNELS = ("qstats", "qtopk", "qpack", "scan", "topb", "gather", "pack", "attn", "append", "qpool")
 
 
 class Heads(ctypes.Structure):
@@ -33,7 +34,8 @@ class Heads(ctypes.Structure):
 
 
 class Params(ctypes.Structure):
-    _fields_ = [("n_q", ctypes.c_int32), ("budget", ctypes.c_int32)]
+    """n_q, budget and the pooling order (KVSEL_POOL_HEAD by default)."""
+    _fields_ = [("n_q", ctypes.c_int32), ("budget", ctypes.c_int32), ("pooling", ctypes.c_int32)]
 
 
 class Cache(ctypes.Structure):

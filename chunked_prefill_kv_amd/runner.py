@@ -30,7 +30,7 @@ def to_host_bits(t: torch.Tensor) -> np.ndarray:
 class PromptRunner:
     """Chunked prefill of one prompt (batch 1) with a contiguous KV cache of capacity L."""
 
-    def __init__(self, wl: gen.Workload, device="cuda", out_dtype=torch.bfloat16):
+    def __init__(self, wl: gen.Workload, device="cuda", out_dtype=torch.bfloat16, pooling: int = K.KVSEL_POOL_HEAD):
         self.wl = wl
         self.device = device
         self.dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -40,7 +40,7 @@ class PromptRunner:
         self.kc = torch.zeros(1, wl.H_kv, wl.L, wl.d, dtype=self.dt, device=device)
         self.vc = torch.zeros_like(self.kc)
         self.h = K.heads(wl.H_q, wl.H_kv, wl.d, K.KVSEL_BF16 if wl.dtype == "bf16" else K.KVSEL_F32)
-        self.p = K.Params(wl.n_q, wl.B)
+        self.p = K.Params(wl.n_q, wl.B, pooling)
         self.cache = K.cache(self.kc, self.vc, wl.L)
         self.prior = torch.tensor(self.starts, dtype=torch.int64, device=device)
         self.batches = [K.batch([t], c, self.prior[i:i + 1]) for i, (t, c) in enumerate(zip(self.starts, self.lens))]
@@ -79,7 +79,8 @@ class PromptRunner:
 class DecodeRunner:
     """One ragged decode step (chunk of 1 per sequence) over a paged KV cache."""
 
-    def __init__(self, wl: gen.Workload, inputs: gen.DecodeInputs, device="cuda", out_dtype=torch.bfloat16):
+    def __init__(self, wl: gen.Workload, inputs: gen.DecodeInputs, device="cuda", out_dtype=torch.bfloat16,
+                 pooling: int = K.KVSEL_POOL_HEAD):
         self.wl = wl
         self.inp = inputs
         self.device = device
@@ -93,7 +94,7 @@ class DecodeRunner:
         self.v_new = to_device(inputs.v_new, device)
         self.prior = to_device(inputs.prior_len, device)
         self.h = K.heads(wl.H_q, wl.H_kv, wl.d, K.KVSEL_BF16 if wl.dtype == "bf16" else K.KVSEL_F32)
-        self.p = K.Params(wl.n_q, wl.B)
+        self.p = K.Params(wl.n_q, wl.B, pooling)
         self.b = K.batch(inputs.prior_len.tolist(), 1, self.prior)
         self.cache = K.cache(self.k_pool, self.v_pool, self.k_pool.shape[0], bs, self.table)
         self.ws = torch.empty(K.workspace_size(self.h, self.b, self.p), dtype=torch.uint8, device=device)

@@ -64,10 +64,25 @@ typedef struct {
     float scale;
 } kvsel_heads;
 
-/* Selection budget.  n_q >= 1 queries kept per query head (all when
- * n_q >= chunk_len); budget >= 1 prior keys kept per KV head. */
+/* Order of the two poolings of step 2.
+ *   KVSEL_POOL_HEAD (0): as above - mean over the group's query heads of each
+ *     head's max over its own kept queries (steps 1-2 as listed).
+ *   KVSEL_POOL_GROUP (1): the group is pooled first.  QuoKA article, Table 4
+ *     caption: the method's cost is stated with the number of KV heads in
+ *     place of the number of query heads.  For every KV head g and chunk
+ *     token i, qbar[g][i] = mean over the G query heads of g of q/|q| (a zero
+ *     row contributes 0); step 1 runs on the pooled rows (n_q tokens kept per
+ *     KV head) and S[g][j] = max over kept i of qbar[g][i] . k_j / |k_j|, the
+ *     max over kept tokens of the mean over heads of the cosine.  With
+ *     chunk_len == 1 both orders give the same score. */
+typedef enum { KVSEL_POOL_HEAD = 0, KVSEL_POOL_GROUP = 1 } kvsel_pooling;
+
+/* Selection budget.  n_q >= 1 queries kept per query head (per KV head with
+ * KVSEL_POOL_GROUP; all when n_q >= chunk_len); budget >= 1 prior keys kept
+ * per KV head; pooling is a kvsel_pooling. */
 typedef struct {
     int32_t n_q, budget;
+    int32_t pooling;
 } kvsel_params;
 
 /* One layer's KV cache.
@@ -113,7 +128,8 @@ kvsel_status kvsel_sparse_attn_workspace_size(const kvsel_heads *heads, const kv
  *           neither.
  *   q_keep  optional debug out [batch][h_q][min(n_q, chunk_len)] int32: the
  *           kept query tokens, ascending; written only for sequences with
- *           T_b > budget.
+ *           T_b > budget.  With KVSEL_POOL_GROUP and chunk_len > 1 the rows
+ *           are per KV head: [batch][h_kv][min(n_q, chunk_len)].
  *   scores  optional debug out [batch][h_kv][score_stride] fp32 with
  *           score_stride = max_b T_b: S[g][j] for j < T_b; written only for
  *           sequences with T_b > budget. */
@@ -169,7 +185,8 @@ typedef enum {
     KVSEL_K_PACK = 6,     /* step 4: compacted keys + chunk keys for attention, and the cache append */
     KVSEL_K_ATTN = 7,     /* step 5: attention */
     KVSEL_K_APPEND = 8,   /* reserved: the cache append runs inside the pack kernel */
-    KVSEL_K_COUNT = 9
+    KVSEL_K_QPOOL = 9,    /* step 1 with KVSEL_POOL_GROUP: the group's unit queries averaged per token */
+    KVSEL_K_COUNT = 10
 } kvsel_kernel;
 
 kvsel_status kvsel_trace_start(uint32_t kernel_mask);

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(K.LIB_PATH)
     for name in _declared():
         assert hasattr(lib, name), name
-    assert K.version() == 100
+    assert K.version() == 101
 
 
 def _bad(h=None, b=None, p=None):
@@ -48,6 +48,7 @@ def _status(h, b, p):
     (dict(h=K.heads(30, 8, 128, K.KVSEL_BF16)), K.KVSEL_ERR_INVALID_ARG),    # h_q % h_kv
     (dict(h=K.heads(32, 0, 128, K.KVSEL_BF16)), K.KVSEL_ERR_INVALID_ARG),
     (dict(h=K.heads(32, 8, 96, K.KVSEL_BF16)), K.KVSEL_ERR_UNSUPPORTED),     # d
+    (dict(p=K.Params(256, 4096, 2)), K.KVSEL_ERR_INVALID_ARG),                # pooling
     (dict(h=K.heads(32, 8, 128, 7)), K.KVSEL_ERR_INVALID_ARG),               # dtype
     (dict(h=K.heads(32, 8, 128, K.KVSEL_BF16, -1.0)), K.KVSEL_ERR_INVALID_ARG),
     (dict(p=K.Params(0, 4096)), K.KVSEL_ERR_INVALID_ARG),                     # n_q

@@ -51,8 +51,10 @@ def _bits(x: np.ndarray) -> np.ndarray:
     return x.view(np.uint32) if x.dtype == np.float32 else x
 
 
-def check_chunk(r: runner.PromptRunner, k: int, chunks, c64, heads=None):
-    """select (with debug outputs) then prefill_chunk for chunk k; every rule on KV heads `heads`."""
+def check_chunk(r: runner.PromptRunner, k: int, chunks, c64, heads=None, pooling="head"):
+    """select (with debug outputs) then prefill_chunk for chunk k; every rule on KV heads `heads`.
+    pooling="group": the kept tokens are per KV head and are checked on the
+    oracle's pooled rows; the scores against the oracle's group-pooled scan."""
     wl = r.wl
     T, C = r.starts[k], r.lens[k]
     Qc, Kc, Vc = c64[k]
@@ -62,7 +64,8 @@ def check_chunk(r: runner.PromptRunner, k: int, chunks, c64, heads=None):
     idx = torch.full((1, wl.H_kv, wl.B), -7, dtype=torch.int32, device=dev)
     ks = torch.empty(1, wl.H_kv, wl.B, wl.d, dtype=r.dt, device=dev)
     vs = torch.empty_like(ks)
-    keep = torch.full((1, wl.H_q, nqp), -7, dtype=torch.int32, device=dev)
+    keep_rows = wl.H_kv if pooling == "group" and C > 1 else wl.H_q
+    keep = torch.full((1, keep_rows, nqp), -7, dtype=torch.int32, device=dev)
     S = torch.full((1, wl.H_kv, max(T, 1)), float("nan"), dtype=torch.float32, device=dev)
     K.kvsel_select(r.h, r.batches[k], r.p, r.chunks[k][0], r.cache, idx, ks, vs, keep, S, r.ws)
     r.run_chunk(k)
@@ -72,7 +75,16 @@ def check_chunk(r: runner.PromptRunner, k: int, chunks, c64, heads=None):
     G = wl.G
     heads = range(wl.H_kv) if heads is None else heads
     qh = [h for g in heads for h in range(g * G, (g + 1) * G)]
-    if T > wl.B:
+    if T > wl.B and keep_rows == wl.H_kv:
+        keep_h = keep[0].cpu().numpy()
+        Qbar = quoka.pooled_queries(Qc, wl.H_kv)
+        S_h = S[0].cpu().numpy()
+        for g in heads:
+            parity.check_keep(Qbar[g], wl.n_q, keep_h[g])
+            S_or = quoka.key_scores_group(Qbar[g:g + 1], [np.sort(keep_h[g])], Kp[g:g + 1])[0]
+            parity.check_close(S_h[g, :T], S_or, parity.S_TOL, f"S chunk {k} head {g}")
+            parity.check_idx(S_or, wl.B, idx_h[g], S_h[g, :T])
+    elif T > wl.B:
         keep_h = keep[0].cpu().numpy()
         for h in qh:
             parity.check_keep(Qc[h], wl.n_q, keep_h[h])
@@ -116,6 +128,28 @@ def test_prefill_matches_oracle(name):
     r.load(chunks, keep_idx=True)
     for k in range(wl.n_chunks):
         check_chunk(r, k, chunks, c64)
+
+
+GROUP = ["bf16_gqa_ragged", "bf16_mqa", "f32_d128", "bf16_d64", "bf16_nq1", "bf16_keep_all_queries", "bf16_g1"]
+
+
+@pytest.mark.parametrize("name", GROUP)
+def test_group_pooled_prefill_matches_oracle(name):
+    """The group-first pooling order (KVSEL_POOL_GROUP) against the oracle's
+    pooling="group" on every chunk: kept tokens of the pooled rows, scores
+    (bf16 caches score the pooled rows as [hi | lo] bf16 pairs), index sets,
+    gather and attention."""
+    wl = SMALL[name] if name in SMALL else LLAMA.replace(L=1500, C=300, H_q=2, H_kv=2, n_q=40, B=400)
+    print(f"[case] group-pooled prefill {name} {wl}", flush=True)
+    chunks = [gen.chunk_inputs(wl, k) for k in range(wl.n_chunks)]
+    if name == "bf16_gqa_ragged":                       # a zero key and a zero query row
+        chunks[0][1][1, 5] = 0
+        chunks[3][0][2, 17] = 0
+    c64 = _f64(chunks)
+    r = runner.PromptRunner(wl, out_dtype=torch.float32, pooling=K.KVSEL_POOL_GROUP)
+    r.load(chunks, keep_idx=True)
+    for k in range(wl.n_chunks):
+        check_chunk(r, k, chunks, c64, pooling="group")
 
 
 def test_needles_are_recalled():
@@ -175,6 +209,33 @@ def test_sparse_attn_given_oracle_set(dtype):
         ref = quoka.attend(Qc, [Kp[g, idx[g][:n]] for g in range(wl.H_kv)],
                            [Vp[g, idx[g][:n]] for g in range(wl.H_kv)], Kc, Vc)
         parity.check_close(O[b], ref, parity.o_tol(dtype), f"sparse_attn seq {b} n_sel {n}")
+
+
+def test_decode_group_pooling_single_token():
+    """With one chunk token the group-first order scores the same as the
+    per-head order (max over one token); the library then takes the per-head
+    path.  Checked against the oracle's group-pooled scores."""
+    wl = gen.WORKLOADS["decode_paged"].replace(batch=4, decode_len_lo=600, decode_len_hi=2000, B=500)
+    print("[case] decode group pooling", flush=True)
+    di = gen.decode_inputs(wl)
+    dr = runner.DecodeRunner(wl, di, out_dtype=torch.float32, pooling=K.KVSEL_POOL_GROUP)
+    T_max = int(di.prior_len.max())
+    S = torch.full((wl.batch, wl.H_kv, T_max), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.full((wl.batch, wl.H_kv, wl.B), -7, dtype=torch.int32, device="cuda")
+    K.kvsel_select(dr.h, dr.b, dr.p, dr.q, dr.cache, idx, None, None, None, S, dr.ws)
+    torch.cuda.synchronize()
+    S_h, idx_h = S.cpu().numpy(), idx.cpu().numpy()
+    for b in range(wl.batch):
+        T = int(di.prior_len[b])
+        if T <= wl.B:
+            continue
+        kp, _ = di.logical_kv(b, wl.block_size)
+        Kp = gen.to_f64(kp)
+        Qbar = quoka.pooled_queries(gen.to_f64(di.q[b]), wl.H_kv)
+        S_or = quoka.key_scores_group(Qbar, [np.array([0])] * wl.H_kv, Kp)
+        for g in range(wl.H_kv):
+            parity.check_close(S_h[b, g, :T], S_or[g], parity.S_TOL, f"S seq {b} head {g}")
+            parity.check_idx(S_or[g], wl.B, idx_h[b, g], S_h[b, g, :T])
 
 
 @pytest.mark.parametrize("variant", ["gqa", "mqa_g32"])
