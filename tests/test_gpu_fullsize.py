@@ -21,7 +21,7 @@ def _gpu():
     K.load()
 
 
-def _sampled_chunk(r, chunks, k, heads):
+def _sampled_chunk(r, chunks, k, heads, pooling="head"):
     """Rules 1-3 and O for chunk k on KV heads `heads`, after chunks < k ran through prefill."""
     wl = r.wl
     T, C = r.starts[k], r.lens[k]
@@ -31,7 +31,8 @@ def _sampled_chunk(r, chunks, k, heads):
     idx = torch.full((1, wl.H_kv, wl.B), -7, dtype=torch.int32, device=dev)
     ks = torch.empty(1, wl.H_kv, wl.B, wl.d, dtype=r.dt, device=dev)
     vs = torch.empty_like(ks)
-    keep = torch.full((1, wl.H_q, nqp), -7, dtype=torch.int32, device=dev)
+    group = pooling == "group" and C > 1
+    keep = torch.full((1, wl.H_kv if group else wl.H_q, nqp), -7, dtype=torch.int32, device=dev)
     S = torch.full((1, wl.H_kv, max(T, 1)), float("nan"), dtype=torch.float32, device=dev)
     K.kvsel_select(r.h, r.batches[k], r.p, r.chunks[k][0], r.cache, idx, ks, vs, keep, S, r.ws)
     r.run_chunk(k)
@@ -47,9 +48,14 @@ def _sampled_chunk(r, chunks, k, heads):
         kp_bits = np.concatenate([c[1][g:g + 1] for c in chunks[:k]], axis=1)
         vp_bits = np.concatenate([c[2][g:g + 1] for c in chunks[:k]], axis=1)
         Kp, Vp = gen.to_f64(kp_bits), gen.to_f64(vp_bits)
-        for i, h in enumerate(range(g * G, (g + 1) * G)):
-            parity.check_keep(Qc[i], wl.n_q, keep_h[h])
-        S_or = quoka.key_scores(Qc, [np.sort(keep_h[h]) for h in range(g * G, (g + 1) * G)], Kp)[0]
+        if group:
+            Qbar = quoka.pooled_queries(Qc, 1)
+            parity.check_keep(Qbar[0], wl.n_q, keep_h[g])
+            S_or = quoka.key_scores_group(Qbar, [np.sort(keep_h[g])], Kp)[0]
+        else:
+            for i, h in enumerate(range(g * G, (g + 1) * G)):
+                parity.check_keep(Qc[i], wl.n_q, keep_h[h])
+            S_or = quoka.key_scores(Qc, [np.sort(keep_h[h]) for h in range(g * G, (g + 1) * G)], Kp)[0]
         parity.check_close(S_h[g, :T], S_or, parity.S_TOL, f"S chunk {k} head {g}")
         parity.check_idx(S_or, wl.B, idx_h[g], S_h[g, :T])
         n = min(wl.B, T)
@@ -76,6 +82,21 @@ def test_fullsize_prefill_sampled(name, sample):
     for k in range(wl.n_chunks):
         if k in sample:
             _sampled_chunk(r, chunks, k, sample[k])
+        else:
+            r.run_chunk(k)
+
+
+def test_fullsize_prefill_group_pooling_sampled():
+    """The bench's 32K layer with the group-first pooling order: a mid and the last chunk."""
+    wl = gen.WORKLOADS["llama8b_32k"]
+    print("[case] full-size group-pooled prefill llama8b_32k", flush=True)
+    chunks = [gen.chunk_inputs(wl, k) for k in range(wl.n_chunks)]
+    r = runner.PromptRunner(wl, out_dtype=torch.bfloat16, pooling=K.KVSEL_POOL_GROUP)
+    r.load(chunks, keep_idx=True)
+    sample = {9: [2], 15: [6]}
+    for k in range(wl.n_chunks):
+        if k in sample:
+            _sampled_chunk(r, chunks, k, sample[k], pooling="group")
         else:
             r.run_chunk(k)
 
