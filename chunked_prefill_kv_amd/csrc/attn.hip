@@ -117,6 +117,12 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
         if (rvalid) raw = *reinterpret_cast<const u32x4*>(q + qoff + 16 * ks + 8 * half);
         qf[ks] = __builtin_bit_cast(bf16x8, raw);
     }
+    // Complete the Q loads here, on every path: otherwise the loop header
+    // merges a path on which they may still be in flight and the compiler's
+    // wait analysis puts a wait for every outstanding load (including the
+    // next tile's, just issued) in front of each tile's first MFMA.
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
 
     const uint16_t* kb = kall + static_cast<int64_t>(bg) * nk_pad * D;
     const uint16_t* vb = vall + static_cast<int64_t>(bg) * D * nk_pad;
@@ -126,13 +132,27 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
     // then.  Buffer (t+1)&1 was last read in tile t-1 and buffer t&1 (K(t+2))
     // in tile t, each closed by a barrier before the write.
     u32x4 rk[PK], rv[PV];
+    // Per-thread byte offsets inside a tile, fixed for the whole loop: a load
+    // is a buffer load with this lane offset and the tile's uniform offset
+    // (no per-load 64-bit address arithmetic on the VALU).
+    uint32_t koff[PK], voff[PV];
+#pragma unroll
+    for (int i = 0; i < PK; ++i) {
+        const int p = tid + NT * i;
+        koff[i] = static_cast<uint32_t>(((p / (D / 8)) * D + (p % (D / 8)) * 8) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < PV; ++i) {
+        const int p = tid + NT * i;
+        voff[i] = static_cast<uint32_t>(((p / (KT / 8)) * nk_pad + (p % (KT / 8)) * 8) * 2);
+    }
+    // buffer descriptors over this KV head's packed K and V^T (reads past the
+    // end return 0); the tile offset is the uniform soffset operand
+    const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kb), 0, nk_pad * D * 2, kBufferFormat);
+    const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vb), 0, nk_pad * D * 2, kBufferFormat);
     auto fetch_k = [&](int t) {
 #pragma unroll
-        for (int i = 0; i < PK; ++i) {
-            const int p = tid + NT * i;
-            const int r = p / (D / 8), c = p % (D / 8);
-            rk[i] = *reinterpret_cast<const u32x4*>(kb + static_cast<int64_t>(t * KT + r) * D + c * 8);
-        }
+        for (int i = 0; i < PK; ++i) rk[i] = __builtin_amdgcn_raw_buffer_load_b128(rsk, koff[i], t * KT * D * 2, 0);
     };
     auto stash_k = [&](int buf) {
 #pragma unroll
@@ -144,11 +164,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
     };
     auto fetch_v = [&](int t) {
 #pragma unroll
-        for (int i = 0; i < PV; ++i) {
-            const int p = tid + NT * i;
-            const int d = p / (KT / 8), j = p % (KT / 8);
-            rv[i] = *reinterpret_cast<const u32x4*>(vb + static_cast<int64_t>(d) * nk_pad + t * KT + j * 8);
-        }
+        for (int i = 0; i < PV; ++i) rv[i] = __builtin_amdgcn_raw_buffer_load_b128(rsv, voff[i], t * KT * 2, 0);
     };
     auto stash_v = [&](int buf) {
 #pragma unroll
@@ -326,21 +342,27 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     };
 
+    // Every fetch and stash is unconditional, with tile indices clamped to the
+    // last tile this workgroup reads (a tile of the packed list, so always in
+    // bounds; the extra copies land in the buffer no one reads next): the same
+    // loads are then in flight on every path, the compiler's waits count them
+    // exactly and each load keeps its full tile of latency.
+    const int t_last = max(t_beg + ntiles - 1, 0);
     if (ntiles > 0) {
         fetch_k(t_beg);
         fetch_v(t_beg);
         stash_k(0);
         stash_v(0);
-        if (ntiles > 1) fetch_k(t_beg + 1);
     }
+    fetch_k(min(t_beg + 1, t_last));
     __syncthreads();
     for (int u = 0; u < ntiles; ++u) {           // u: tile within this workgroup's range
         const int t = t_beg + u;
         const int buf = u & 1;
-        if (u + 1 < ntiles) fetch_v(t + 1);
+        fetch_v(min(t + 1, t_last));
         auto mid = [&] {
             if (u + 1 < ntiles) stash_k(buf ^ 1);
-            if (u + 2 < ntiles) fetch_k(t + 2);
+            fetch_k(min(t + 2, t_last));
         };
         const int s0 = t * KT;
         if (wave_active && s0 <= n_s + w_tmax) {

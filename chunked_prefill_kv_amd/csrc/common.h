@@ -13,6 +13,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+// Word 3 of a raw buffer resource (untyped loads/stores, 32-bit data format).
+constexpr int kBufferFormat = 0x00020000;
+
 // ---------------------------------------------------------------- element access
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
