@@ -144,6 +144,12 @@ kvsel_status check_cache(const kvsel_cache* c, const kvsel_batch* b, int extra) 
     return KVSEL_OK;
 }
 
+// The gathering attention carries cache row numbers as int32.
+bool cache_rows_fit(const kvsel_cache* c, const kvsel_heads* h, const kvsel_batch* b) {
+    const int64_t per = c->block_size == 0 ? int64_t(b->batch) * c->capacity : c->capacity * c->block_size;
+    return per * h->h_kv < (int64_t(1) << 31);
+}
+
 CacheView make_view(const kvsel_cache* c, const kvsel_heads* h) {
     CacheView v;
     v.k = static_cast<char*>(c->k);
@@ -195,7 +201,7 @@ SelShape pooled_shape(const SelShape& s) {
 // ----------------------------------------------------------------------------- workspace layout
 
 struct Layout {
-    size_t qpart, qcos, qrn, keep, qsel, rq, qbar, scores, topb, idx, nsel, kall, vall, apart, total;
+    size_t qpart, qcos, qrn, keep, qsel, rq, qbar, scores, topb, idx, rowidx, nsel, kall, vall, apart, total;
     int nk_pad;
 };
 
@@ -220,6 +226,7 @@ Layout layout(const SelShape& s, bool with_attn) {
     L.scores = take(bg * (s.t_max > 0 ? s.t_max : 1) * 4 * s.nsplit);
     L.topb = take(topb_scratch_bytes(static_cast<int>(bg), s.t_max, s.budget));
     L.idx = take(bg * s.budget * 4);
+    L.rowidx = take(bg * s.budget * 4);
     L.nsel = take(size_t(s.batch) * 4);
     const int64_t nsel_max = s.budget < s.t_max ? s.budget : s.t_max;
     L.nk_pad = static_cast<int>(round_up(nsel_max + s.C, 64));
@@ -243,7 +250,8 @@ kvsel_status check_ws(void* ws, size_t have, size_t need) {
 
 // Steps 1-3 into idx (shared by select and prefill_chunk).
 kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, const CacheView& cv, void* ws,
-                        const Layout& L, int32_t* idx, int32_t* q_keep, float* scores, hipStream_t st) {
+                        const Layout& L, int32_t* idx, int32_t* q_keep, float* scores, hipStream_t st,
+                        int32_t* rowidx = nullptr) {
     bool any = false;
     for (int i = 0; i < b->batch; ++i) any |= b->prior_len_host[i] > s.budget;
     const int64_t* T = b->prior_len_dev;
@@ -276,7 +284,8 @@ kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, 
     }
     float* comb = scores ? scores : S;
     KVSEL_TRY(traced(KVSEL_K_TOPB, st, [&] { return launch_topb(s.batch * s.h_kv, s.h_kv, S, sc.nsplit, split_stride, comb, s.t_max, T,
-                                                                s.budget, s.t_max, any, at<uint32_t>(ws, L.topb), idx, st); }), "key top-B");
+                                                                s.budget, s.t_max, any, at<uint32_t>(ws, L.topb), idx, st,
+                                                                rowidx ? &cv : nullptr, rowidx); }), "key top-B");
     return KVSEL_OK;
 }
 
@@ -428,7 +437,9 @@ kvsel_status kvsel_prefill_chunk(const kvsel_heads* heads, const kvsel_batch* ba
     const CacheView cv = make_view(cache, heads);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     int32_t* idx_buf = idx ? idx : at<int32_t>(workspace, L.idx);
-    if ((st = run_select(s, batch, q, cv, workspace, L, idx_buf, nullptr, nullptr, hs))) return st;
+    const bool gather = attn_use_gather(s) && cache_rows_fit(cache, heads, batch);
+    int32_t* rowidx = gather ? at<int32_t>(workspace, L.rowidx) : nullptr;
+    if ((st = run_select(s, batch, q, cv, workspace, L, idx_buf, nullptr, nullptr, hs, rowidx))) return st;
     PackSrc src{};
     src.cache = &cv;
     src.prior_len = batch->prior_len_dev;
@@ -438,11 +449,21 @@ kvsel_status kvsel_prefill_chunk(const kvsel_heads* heads, const kvsel_batch* ba
     src.append = true;
     int32_t* nsel = at<int32_t>(workspace, L.nsel);
     const float scale = heads->scale > 0.0f ? heads->scale : 1.0f / std::sqrt(static_cast<float>(heads->d));
+    if (gather) {
+        // fused gather: the attention reads the kept rows from the cache itself
+        // (row numbers from the top-B); the append runs on its own (it writes
+        // rows [T_b, T_b + C), which neither the selection nor the attention reads)
+        AttnGather ga{cv, batch->prior_len_dev, s.budget, rowidx, s.budget, k_chunk, v_chunk};
+        KVSEL_TRY(traced(KVSEL_K_ATTN, hs, [&] { return launch_attn(s, q, nullptr, nullptr, nullptr, 0, scale, out, out_dtype == KVSEL_F32,
+                              at<float>(workspace, L.apart), hs, &ga); }), "attention");
+        KVSEL_TRY(traced(KVSEL_K_APPEND, hs, [&] { return launch_append(s, cv, batch->prior_len_dev, k_chunk, v_chunk, hs); }), "cache append");
+        return KVSEL_OK;
+    }
     KVSEL_TRY(traced(KVSEL_K_PACK, hs, [&] { return launch_pack(s, src, k_chunk, v_chunk, L.nk_pad, at<void>(workspace, L.kall), at<void>(workspace, L.vall),
                           nsel, hs); }), "pack");
     KVSEL_TRY(traced(KVSEL_K_ATTN, hs, [&] { return launch_attn(s, q, at<void>(workspace, L.kall), at<void>(workspace, L.vall), nsel, L.nk_pad, scale, out,
                           out_dtype == KVSEL_F32, at<float>(workspace, L.apart), hs); }), "attention");
-    // the cache append happens inside the pack kernel (it reads the chunk's rows anyway)
+    // here the cache append happens inside the pack kernel (it reads the chunk's rows anyway)
     return KVSEL_OK;
 }
 

@@ -59,26 +59,35 @@ __device__ __forceinline__ int sigma(int m) {
 #ifndef KVSEL_ATTN_PIPE
 #define KVSEL_ATTN_PIPE 0
 #endif
+#ifndef KVSEL_ATTN_GATHER
+#define KVSEL_ATTN_GATHER 1               // gathering attention for single-row-block KV heads
+#endif
 
-template <int D, bool OUT_F32, int KT, int WAVES>
+//
+// GATHER: the key list is read from its sources (kept cache rows through idx,
+// then the chunk's rows) instead of the packed copy; V then arrives row-major
+// and is staged [key][d], its V^T fragments read with LDS transpose loads.
+template <int D, bool OUT_F32, int KT, int WAVES, bool GATHER>
 __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ kall,
                                                            const uint16_t* __restrict__ vall,
                                                            const int32_t* __restrict__ nsel, int nk_pad, int C, int G,
                                                            int h_kv, int row_blocks, float cl2,
                                                            void* __restrict__ out, int ksplit,
-                                                           float* __restrict__ part) {
+                                                           float* __restrict__ part, AttnGather ga) {
+    constexpr bool VR = GATHER;             // V tile staged row-major
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
     constexpr int NKB = KT / 32;            // 32-key MFMA blocks per tile
     constexpr int LDK = D + 8;
-    constexpr int LDV = KT + 8;
+    constexpr int LDV = VR ? D + 16 : KT + 8;   // V tile row: [key][d] (pitch spreads a transpose
+                                                 // load over 4 bank groups) or [d][key]
     constexpr int NT = 64 * WAVES;          // threads per workgroup
     constexpr int ROWS = 32 * WAVES;        // query rows per workgroup
     constexpr int PK = KT * D / 8 / NT;     // 16-byte K pieces per thread per tile
     constexpr int PV = D * KT / 8 / NT;     // 16-byte V^T pieces per thread per tile
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * LDV];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][VR ? KT * LDV : D * LDV];
 
     // slot -> (KV head, row block, key split); later row blocks (more keys) first
     const int slot = xcd_slot(blockIdx.x, gridDim.x);
@@ -88,7 +97,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
     const int ksp = rem % ksplit;
     const int b = bg / h_kv, g = bg % h_kv;
     const int nrows = G * C;
-    const int n_s = nsel[b];
+    const int64_t T_b = GATHER ? ga.prior_len[b] : 0;
+    const int n_s = GATHER ? static_cast<int>(T_b < ga.budget ? T_b : ga.budget) : nsel[b];
     const int row_wg0 = rblk * ROWS;
     const int wg_tmax = min(row_wg0 + ROWS - 1, nrows - 1) / G;
     const int ntiles_all = (n_s + wg_tmax + 1 + KT - 1) / KT;
@@ -154,6 +164,30 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
 #pragma unroll
         for (int i = 0; i < PK; ++i) rk[i] = __builtin_amdgcn_raw_buffer_load_b128(rsk, koff[i], t * KT * D * 2, 0);
     };
+    // Gathering: slot s < n_s is cache row rowidx[s], then the chunk's rows
+    // (coded -1 - chunk row); slots past the list read the chunk's last row
+    // (finite values that the causal mask removes).  The row numbers of the
+    // next two tiles are held in registers (R1: tile t+1, R2: tile t+2 at the
+    // start of tile t), so no row load waits on an index load.
+    int32_t R1[PK], R2[PK];
+    auto rows_of = [&](int t, int32_t (&rr)[PK]) {
+#pragma unroll
+        for (int i = 0; i < PK; ++i) {
+            const int sl = t * KT + (tid + NT * i) / (D / 8);
+            rr[i] = sl < n_s ? ga.rowidx[static_cast<int64_t>(bg) * ga.ri_stride + sl]
+                             : -1 - (bg * C + min(sl - n_s, C - 1));
+        }
+    };
+    auto gfetch = [&](const int32_t (&rr)[PK], bool v, u32x4 (&dst)[PK]) {
+#pragma unroll
+        for (int i = 0; i < PK; ++i) {
+            const int32_t r = rr[i];
+            const char* base = r >= 0 ? (v ? ga.cv.v : ga.cv.k) + static_cast<int64_t>(r) * (D * 2)
+                                      : static_cast<const char*>(v ? ga.v_chunk : ga.k_chunk) +
+                                            static_cast<int64_t>(-1 - r) * (D * 2);
+            dst[i] = *reinterpret_cast<const u32x4*>(base + ((tid + NT * i) % (D / 8)) * 16);
+        }
+    };
     auto stash_k = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < PK; ++i) {
@@ -170,9 +204,35 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
 #pragma unroll
         for (int i = 0; i < PV; ++i) {
             const int p = tid + NT * i;
-            const int d = p / (KT / 8), j = p % (KT / 8);
-            *reinterpret_cast<u32x4*>(&v_lds[buf][d * LDV + j * 8]) = rv[i];
+            if (VR) {
+                const int r = p / (D / 8), c = p % (D / 8);
+                *reinterpret_cast<u32x4*>(&v_lds[buf][r * LDV + c * 8]) = rv[i];
+            } else {
+                const int d = p / (KT / 8), j = p % (KT / 8);
+                *reinterpret_cast<u32x4*>(&v_lds[buf][d * LDV + j * 8]) = rv[i];
+            }
         }
+    };
+    // V^T fragment of the P.V MFMA: d = 32*db + (lane & 31), keys kb + 8*half
+    // .. +7.  Row-major V: two transpose loads; in each 16-lane group, lane j
+    // receives element (j & 3) of the 8 bytes addressed by lanes 4r + (j >> 2),
+    // r = 0..3, so lane s of the group points at key kb + 8*half + (s >> 2),
+    // d = 32*db + 16*((lane >> 4) & 1) + 4*(s & 3), and gets keys +0..3 of
+    // column d (+4..7 from the second load).
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef short v8s __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    auto vfrag = [&](int buf, int db, int k0) -> bf16x8 {
+        if (VR) {
+            const int j = lane & 15;
+            const int row = k0 + 8 * half + (j >> 2);
+            const int colv = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+            const v4s x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)&v_lds[buf][row * LDV + colv]);
+            const v4s x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)&v_lds[buf][(row + 4) * LDV + colv]);
+            const v8s x = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            return __builtin_bit_cast(bf16x8, x);
+        }
+        return *reinterpret_cast<const bf16x8*>(&v_lds[buf][(32 * db + col) * LDV + k0 + 8 * half]);
     };
 
     f32x16 o[DB];
@@ -213,7 +273,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int k16 = 0; k16 < 2; ++k16)
-                    vf[db][k16] = *reinterpret_cast<const bf16x8*>(&v_lds[buf][(32 * db + col) * LDV + 32 * kb2 + 16 * k16 + 8 * half]);
+                    vf[db][k16] = vfrag(buf, db, 32 * kb2 + 16 * k16);
             // register r holds slot s0 + 32*kb2 + 16*(r>>3) + 8*half + (r&7)
             if (MASK) {
 #pragma unroll
@@ -309,7 +369,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int k16 = 0; k16 < 2; ++k16)
-                    vf[db][k16] = *reinterpret_cast<const bf16x8*>(&v_lds[buf][(32 * db + col) * LDV + 32 * kb2 + 16 * k16 + 8 * half]);
+                    vf[db][k16] = vfrag(buf, db, 32 * kb2 + 16 * k16);
             bf16x8 pf[2];
 #pragma unroll
             for (int k16 = 0; k16 < 2; ++k16) {
@@ -342,27 +402,50 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     };
 
-    // Every fetch and stash is unconditional, with tile indices clamped to the
-    // last tile this workgroup reads (a tile of the packed list, so always in
-    // bounds; the extra copies land in the buffer no one reads next): the same
-    // loads are then in flight on every path, the compiler's waits count them
-    // exactly and each load keeps its full tile of latency.
+    // Every prefetch is unconditional, with its tile index clamped to the last
+    // tile this workgroup reads (always in bounds; the extra copy is never
+    // stashed): the same loads are then in flight on every path, so the
+    // compiler's waits count them exactly and each load keeps its full tile of
+    // latency.
     const int t_last = max(t_beg + ntiles - 1, 0);
-    if (ntiles > 0) {
-        fetch_k(t_beg);
-        fetch_v(t_beg);
-        stash_k(0);
-        stash_v(0);
+    auto tc = [&](int t) { return min(t, t_last); };
+    if constexpr (GATHER) {
+        static_assert(PK == PV, "K and V rows are fetched together");
+        rows_of(tc(t_beg), R1);
+        if (ntiles > 0) {
+            gfetch(R1, false, rk);
+            gfetch(R1, true, rv);
+            stash_k(0);
+            stash_v(0);
+        }
+        rows_of(tc(t_beg + 1), R1);
+        gfetch(R1, false, rk);
+        rows_of(tc(t_beg + 2), R2);
+    } else {
+        if (ntiles > 0) {
+            fetch_k(t_beg);
+            fetch_v(t_beg);
+            stash_k(0);
+            stash_v(0);
+        }
+        fetch_k(tc(t_beg + 1));
     }
-    fetch_k(min(t_beg + 1, t_last));
     __syncthreads();
     for (int u = 0; u < ntiles; ++u) {           // u: tile within this workgroup's range
         const int t = t_beg + u;
         const int buf = u & 1;
-        fetch_v(min(t + 1, t_last));
+        if constexpr (GATHER) {
+            gfetch(R1, true, rv);                // V(t+1)
+#pragma unroll
+            for (int i = 0; i < PK; ++i) R1[i] = R2[i];
+            rows_of(tc(t + 3), R2);
+        } else {
+            fetch_v(tc(t + 1));
+        }
         auto mid = [&] {
             if (u + 1 < ntiles) stash_k(buf ^ 1);
-            fetch_k(min(t + 2, t_last));
+            if constexpr (GATHER) gfetch(R1, false, rk);   // K(t+2)
+            else fetch_k(tc(t + 2));
         };
         const int s0 = t * KT;
         if (wave_active && s0 <= n_s + w_tmax) {
@@ -527,8 +610,13 @@ __global__ __launch_bounds__(128) void attn_valu_kernel(const float* __restrict_
 
 // ----------------------------------------------------------------------------- launcher
 
+bool attn_use_gather(const SelShape& s) { return KVSEL_ATTN_GATHER && s.esz == 2 && s.G * s.C <= 128; }
+
 int attn_ksplit(const SelShape& s) {
     if (s.esz != 2) return 1;
+    // gathering workgroups wait on dependent loads (index, block table, row):
+    // four shorter key ranges per row block keep more of them in flight
+    if (attn_use_gather(s)) return 4;
     const int64_t wgs = int64_t(s.batch) * s.h_kv * ((s.G * s.C + 127) / 128);
     int k = 1;
     while (k < 4 && wgs * k < 512) k *= 2;            // at least two workgroups per CU
@@ -543,20 +631,26 @@ size_t attn_part_bytes(const SelShape& s) {
 }
 
 hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const void* vall, const int32_t* nsel,
-                       int nk_pad, float scale, void* out, bool out_f32, float* part, hipStream_t st) {
+                       int nk_pad, float scale, void* out, bool out_f32, float* part, hipStream_t st,
+                       const AttnGather* gather) {
     const int bgs = s.batch * s.h_kv;
     if (s.esz == 2) {
         // 8-wave workgroups share one staged copy of every K/V tile; fall back to
         // 4 waves when that would leave fewer than 256 workgroups
         const int rb8 = (s.G * s.C + 255) / 256, rb4 = (s.G * s.C + 127) / 128;
-        const bool w8 = KVSEL_ATTN_WAVES == 8 && bgs * rb8 >= 256;
+        const bool w8 = !gather && KVSEL_ATTN_WAVES == 8 && bgs * rb8 >= 256;
         const int row_blocks = w8 ? rb8 : rb4;
         const int ksplit = w8 ? 1 : attn_ksplit(s);
         dim3 grid(bgs * row_blocks * ksplit), block(w8 ? 512 : 256);
         const float cl2 = scale * 1.4426950408889634f;
         const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)kall, *vv = (const uint16_t*)vall;
-#define KVSEL_ATTN(D, F32, W) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, KVSEL_ATTN_KT, W>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part)
-        if (s.d == 128) {
+        const AttnGather ga = gather ? *gather : AttnGather{};
+#define KVSEL_ATTN(D, F32, W) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, KVSEL_ATTN_KT, W, false>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part, ga)
+#define KVSEL_ATTN_G(D, F32) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, KVSEL_ATTN_KT, 4, true>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part, ga)
+        if (gather) {
+            if (s.d == 128) { if (out_f32) KVSEL_ATTN_G(128, true); else KVSEL_ATTN_G(128, false); }
+            else { if (out_f32) KVSEL_ATTN_G(64, true); else KVSEL_ATTN_G(64, false); }
+        } else if (s.d == 128) {
             if (w8) { if (out_f32) KVSEL_ATTN(128, true, 8); else KVSEL_ATTN(128, false, 8); }
             else { if (out_f32) KVSEL_ATTN(128, true, 4); else KVSEL_ATTN(128, false, 4); }
         } else {
@@ -564,6 +658,7 @@ hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const
             else { if (out_f32) KVSEL_ATTN(64, true, 4); else KVSEL_ATTN(64, false, 4); }
         }
 #undef KVSEL_ATTN
+#undef KVSEL_ATTN_G
         if (ksplit > 1) {
             const int64_t rows = int64_t(s.batch) * s.h_q * s.C;
             const dim3 mg(static_cast<unsigned>((rows * (s.d / 4) + 255) / 256));

@@ -57,6 +57,12 @@ struct CacheView {
     int32_t h_kv;
     int32_t row_bytes;        // d * element bytes
 
+    // row number (row_offset / row_bytes)
+    __device__ __forceinline__ int64_t row_index(int b, int g, int64_t pos) const {
+        if (block_size == 0) return (static_cast<int64_t>(b) * h_kv + g) * capacity + pos;
+        const int64_t blk = block_table[static_cast<int64_t>(b) * max_blocks + pos / block_size];
+        return (blk * h_kv + g) * block_size + pos % block_size;
+    }
     __device__ __forceinline__ int64_t row_offset(int b, int g, int64_t pos) const {
         if (block_size == 0) {
             return ((static_cast<int64_t>(b) * h_kv + g) * capacity + pos) * row_bytes;

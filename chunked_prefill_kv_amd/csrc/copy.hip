@@ -169,6 +169,33 @@ __global__ __launch_bounds__(256) void gather_kernel(CacheView cv, const int64_t
     }
 }
 
+// Cache append on its own (the gathering attention path packs nothing):
+// K/V rows t < C of (b, g) to cache positions T_b + t.
+__global__ __launch_bounds__(256) void append_kernel(CacheView cv, const int64_t* __restrict__ prior_len,
+                                                     const char* __restrict__ k_chunk, const char* __restrict__ v_chunk,
+                                                     int C, int h_kv, int tiles) {
+    const int bg = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+    const int b = bg / h_kv, g = bg % h_kv;
+    const int64_t T = prior_len[b];
+    const int ppr = cv.row_bytes / 16;
+    for (int p = threadIdx.x; p < kTile * ppr; p += 256) {
+        const int t = tile * kTile + p / ppr, c = p % ppr;
+        if (t >= C) continue;
+        const int64_t src = (static_cast<int64_t>(bg) * C + t) * cv.row_bytes;
+        const int64_t dst = cv.row_offset(b, g, T + t);
+        reinterpret_cast<u32x4*>(cv.k + dst)[c] = reinterpret_cast<const u32x4*>(k_chunk + src)[c];
+        reinterpret_cast<u32x4*>(cv.v + dst)[c] = reinterpret_cast<const u32x4*>(v_chunk + src)[c];
+    }
+}
+
+hipError_t launch_append(const SelShape& s, const CacheView& cv, const int64_t* prior_len, const void* k_chunk,
+                         const void* v_chunk, hipStream_t st) {
+    const int tiles = (s.C + kTile - 1) / kTile;
+    hipLaunchKernelGGL(append_kernel, dim3(s.batch * s.h_kv * tiles), dim3(256), 0, st, cv, prior_len,
+                       static_cast<const char*>(k_chunk), static_cast<const char*>(v_chunk), s.C, s.h_kv, tiles);
+    return hipGetLastError();
+}
+
 hipError_t launch_pack(const SelShape& s, const PackSrc& src, const void* k_chunk, const void* v_chunk, int nk_pad,
                        void* kall, void* vall, int32_t* nsel_out, hipStream_t st) {
     PackArgs a;

@@ -57,7 +57,8 @@ hipError_t launch_topk(int problems, int heads_per_seq, const float* scores, int
 
 // Per-KV-head top-B of the (split-partial) key scores on many workgroups:
 // writes out[p][0..budget) (kept indices ascending, -1 past T_p) for every
-// problem p = b * heads_per_seq + g.  comb receives the summed scores (may be
+// problem p = b * heads_per_seq + g, and with cv / rowidx given the cache row
+// number of every kept position (rowidx[p][r], for the gathering attention).  comb receives the summed scores (may be
 // `part` itself).  scratch: topb_scratch_bytes(); its histogram part
 // (problems * 4096 uint32 at its start) must be zero on entry when
 // any_select (launch_qstats clears it).
@@ -65,7 +66,8 @@ int topb_segments(int64_t t_max, int64_t budget);
 size_t topb_scratch_bytes(int problems, int64_t t_max, int64_t budget);
 hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int nsplit, int64_t split_stride,
                        float* comb, int64_t s_stride, const int64_t* prior_len, int64_t budget, int64_t t_max,
-                       bool any_select, uint32_t* scratch, int32_t* out, hipStream_t st);
+                       bool any_select, uint32_t* scratch, int32_t* out, hipStream_t st,
+                       const CacheView* cv = nullptr, int32_t* rowidx = nullptr);
 
 // Gather the kept query rows of every head into Q_sel[b][g][hh*nq_pad + r][d]
 // (raw rows) and rq = 1/|q|; rows r >= nqp repeat row 0 of that head.
@@ -117,14 +119,36 @@ struct PackSrc {
 hipError_t launch_pack(const SelShape& s, const PackSrc& src, const void* k_chunk, const void* v_chunk,
                        int nk_pad, void* kall, void* vall, int32_t* nsel_out, hipStream_t st);
 
-// Step 5 over the packed layout; out is fp32 (out_f32) or bf16.  When the
-// grid would hold fewer than two workgroups per CU the key tiles of every row
-// block are split over attn_ksplit(s) workgroups whose partials (fp32 scratch
-// `part` of attn_part_bytes(s) bytes) a merge kernel combines.
+// Gathering attention: the key list is read straight from its sources, slot
+// s < n_b = min(T_b, budget) from cache row rowidx[b][g][s] (row number as
+// written by launch_topb), the chunk's rows after it, no packed copy.
+struct AttnGather {
+    CacheView cv;
+    const int64_t* prior_len;
+    int64_t budget;
+    const int32_t* rowidx;
+    int64_t ri_stride;
+    const void* k_chunk;             // [b][h_kv][C][d]
+    const void* v_chunk;
+};
+// bf16 KV heads with a single 128-row block (G * C <= 128: decode, short
+// chunks) take the gathering attention: each key row is read by one workgroup
+// only, so packing it first is pure extra traffic.
+bool attn_use_gather(const SelShape& s);
+
+// Step 5 (packed layout, or gathering when `gather` is given); out is fp32
+// (out_f32) or bf16.  When the grid would hold fewer than two workgroups per
+// CU (gathering: always) the key tiles of every row block are split over
+// attn_ksplit(s) workgroups whose partials (fp32 scratch `part` of
+// attn_part_bytes(s) bytes) a merge kernel combines.
 int attn_ksplit(const SelShape& s);
 size_t attn_part_bytes(const SelShape& s);
 hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const void* vall,
                        const int32_t* nsel, int nk_pad, float scale, void* out, bool out_f32,
-                       float* part, hipStream_t st);
+                       float* part, hipStream_t st, const AttnGather* gather = nullptr);
+
+// Cache append without packing: chunk rows -> cache rows [T_b, T_b + C).
+hipError_t launch_append(const SelShape& s, const CacheView& cv, const int64_t* prior_len, const void* k_chunk,
+                         const void* v_chunk, hipStream_t st);
 
 }  // namespace kvsel

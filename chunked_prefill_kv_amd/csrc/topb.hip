@@ -42,6 +42,8 @@ struct TopbArgs {
     uint32_t* thr;            // [problem][2]: tau, need_eq
     uint32_t* segc;           // [problem][nseg][2]: kept above tau, equal to tau
     int32_t* out;             // [problem][budget]
+    CacheView cv;             // with rowidx: the cache the positions index
+    int32_t* rowidx;          // optional [problem][budget]: cache row number of each kept position
 };
 
 }  // namespace
@@ -213,10 +215,13 @@ __global__ __launch_bounds__(256) void topb_write_kernel(TopbArgs a) {
     const int64_t T64 = a.prior_len[p / a.heads_per_seq];
     int32_t* o = a.out + static_cast<int64_t>(p) * a.budget;
     const int j0 = seg * kSeg;
+    const int bq = p / a.heads_per_seq, gq = p % a.heads_per_seq;
+    int32_t* ri = a.rowidx ? a.rowidx + static_cast<int64_t>(p) * a.budget : nullptr;
     if (T64 <= a.budget) {                     // everything is kept: iota, then -1 up to budget
         for (int i = threadIdx.x; i < kSeg; i += 256) {
             const int64_t j = j0 + i;
             if (j < a.budget) o[j] = j < T64 ? static_cast<int32_t>(j) : -1;
+            if (ri && j < T64) ri[j] = static_cast<int32_t>(a.cv.row_index(bq, gq, j));
         }
         return;
     }
@@ -261,7 +266,10 @@ __global__ __launch_bounds__(256) void topb_write_kernel(TopbArgs a) {
         const uint64_t bgt = __ballot(gt), beq = __ballot(eq);
         const uint32_t gb = gt_run + __popcll(bgt & lt), eb = eq_run + __popcll(beq & lt);
         const uint32_t pos = gt ? gb + min(eb, need_eq) : gb + eb;
-        if ((gt || (eq && eb < need_eq)) && pos < static_cast<uint32_t>(a.budget)) o[pos] = j;
+        if ((gt || (eq && eb < need_eq)) && pos < static_cast<uint32_t>(a.budget)) {
+            o[pos] = j;
+            if (ri) ri[pos] = static_cast<int32_t>(a.cv.row_index(bq, gq, j));
+        }
         gt_run += __popcll(bgt);
         eq_run += __popcll(beq);
     }
@@ -279,8 +287,11 @@ size_t topb_scratch_bytes(int problems, int64_t t_max, int64_t budget) {
 
 hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int nsplit, int64_t split_stride,
                        float* comb, int64_t s_stride, const int64_t* prior_len, int64_t budget, int64_t t_max,
-                       bool any_select, uint32_t* scratch, int32_t* out, hipStream_t st) {
+                       bool any_select, uint32_t* scratch, int32_t* out, hipStream_t st, const CacheView* cv,
+                       int32_t* rowidx) {
     TopbArgs a;
+    a.cv = cv ? *cv : CacheView{};
+    a.rowidx = cv ? rowidx : nullptr;
     a.part = part;
     a.nsplit = nsplit;
     a.split_stride = split_stride;

@@ -184,7 +184,7 @@ typedef enum {
     KVSEL_K_GATHER = 5,   /* step 4 (kvsel_select): k_sel/v_sel rows */
     KVSEL_K_PACK = 6,     /* step 4: compacted keys + chunk keys for attention, and the cache append */
     KVSEL_K_ATTN = 7,     /* step 5: attention */
-    KVSEL_K_APPEND = 8,   /* reserved: the cache append runs inside the pack kernel */
+    KVSEL_K_APPEND = 8,   /* cache append on its own (gathering attention path; otherwise inside the pack kernel) */
     KVSEL_K_QPOOL = 9,    /* step 1 with KVSEL_POOL_GROUP: the group's unit queries averaged per token */
     KVSEL_K_COUNT = 10
 } kvsel_kernel;
