@@ -306,3 +306,69 @@ def test_bitwise_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("C,Ts,B", [
+    (200, [0, 400, 1600], 600),        # packed attention (G*C = 800): no prior, T <= B, selection
+    (30, [0, 60, 300], 90),            # gathering attention (G*C = 120)
+])
+def test_batched_prefill_ragged(C, Ts, B):
+    """Several sequences in one kvsel_prefill_chunk call, each with its own
+    prior length (an empty cache, T <= B, T > B): every sequence against the
+    oracle on its own, and its chunk appended to the cache bit for bit."""
+    wl = LLAMA.replace(L=max(Ts) + C, C=C, H_q=8, H_kv=2, n_q=24, B=B)
+    print(f"[case] batched prefill C={C} T={Ts}", flush=True)
+    nb, cap = len(Ts), max(Ts) + C
+    cur = [gen.chunk_inputs(wl, T // C, seq=s) for s, T in enumerate(Ts)]
+    prior = [[gen.chunk_inputs(wl, k, seq=s) for k in range(T // C)] for s, T in enumerate(Ts)]
+    kc = np.zeros((nb, wl.H_kv, cap, wl.d), dtype=np.uint16)
+    vc = np.zeros_like(kc)
+    for s, T in enumerate(Ts):
+        if T:
+            kc[s, :, :T] = np.concatenate([c[1] for c in prior[s]], axis=1)
+            vc[s, :, :T] = np.concatenate([c[2] for c in prior[s]], axis=1)
+    dev = "cuda"
+    kc_d, vc_d = runner.to_device(kc, dev), runner.to_device(vc, dev)
+    q = runner.to_device(np.stack([c[0] for c in cur]), dev)
+    kn = runner.to_device(np.stack([c[1] for c in cur]), dev)
+    vn = runner.to_device(np.stack([c[2] for c in cur]), dev)
+    h = K.heads(wl.H_q, wl.H_kv, wl.d, K.KVSEL_BF16)
+    p = K.Params(wl.n_q, wl.B)
+    prior_d = torch.tensor(Ts, dtype=torch.int64, device=dev)
+    b = K.batch(Ts, C, prior_d)
+    cache = K.cache(kc_d, vc_d, cap)
+    ws = torch.empty(K.workspace_size(h, b, p), dtype=torch.uint8, device=dev)
+    nqp = min(wl.n_q, C)
+    idx = torch.full((nb, wl.H_kv, B), -7, dtype=torch.int32, device=dev)
+    keep = torch.full((nb, wl.H_q, nqp), -7, dtype=torch.int32, device=dev)
+    S = torch.full((nb, wl.H_kv, max(Ts)), float("nan"), dtype=torch.float32, device=dev)
+    K.kvsel_select(h, b, p, q, cache, idx, None, None, keep, S, ws)
+    out = torch.empty(nb, wl.H_q, C, wl.d, dtype=torch.float32, device=dev)
+    idx2 = torch.full_like(idx, -7)
+    K.kvsel_prefill_chunk(h, b, p, q, kn, vn, cache, out, idx2, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), idx2.cpu().numpy())
+    kc_after, vc_after = runner.to_host_bits(kc_d), runner.to_host_bits(vc_d)
+    O = out.double().cpu().numpy()
+    G = wl.G
+    for s, T in enumerate(Ts):
+        assert np.array_equal(kc_after[s, :, T:T + C], cur[s][1]) and np.array_equal(vc_after[s, :, T:T + C], cur[s][2])
+        assert np.array_equal(kc_after[s, :, :T], kc[s, :, :T]), "prior rows must stay untouched"
+        Qc, Kn, Vn = (gen.to_f64(x) for x in cur[s])
+        Kp, Vp = gen.to_f64(kc[s, :, :T]), gen.to_f64(vc[s, :, :T])
+        idx_h = idx[s].cpu().numpy()
+        if T > B:
+            keep_h = keep[s].cpu().numpy()
+            for hh in range(wl.H_q):
+                parity.check_keep(Qc[hh], wl.n_q, keep_h[hh])
+            S_or = quoka.key_scores(Qc, [np.sort(keep_h[hh]) for hh in range(wl.H_q)], Kp)
+            for g in range(wl.H_kv):
+                parity.check_close(S[s, g, :T].cpu().numpy(), S_or[g], parity.S_TOL, f"S seq {s} head {g}")
+                parity.check_idx(S_or[g], B, idx_h[g], S[s, g, :T].cpu().numpy())
+        else:
+            for g in range(wl.H_kv):
+                assert np.array_equal(idx_h[g, :T], np.arange(T)) and np.all(idx_h[g, T:] == -1)
+        n = min(B, T)
+        O_or = quoka.attend(Qc, [Kp[g, idx_h[g, :n]] for g in range(wl.H_kv)],
+                            [Vp[g, idx_h[g, :n]] for g in range(wl.H_kv)], Kn, Vn)
+        parity.check_close(O[s], O_or, parity.o_tol(wl.dtype), f"O seq {s}")
