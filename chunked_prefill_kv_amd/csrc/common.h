@@ -60,15 +60,17 @@ struct CacheView {
     // row number (row_offset / row_bytes)
     __device__ __forceinline__ int64_t row_index(int b, int g, int64_t pos) const {
         if (block_size == 0) return (static_cast<int64_t>(b) * h_kv + g) * capacity + pos;
-        const int64_t blk = block_table[static_cast<int64_t>(b) * max_blocks + pos / block_size];
-        return (blk * h_kv + g) * block_size + pos % block_size;
+        const uint32_t p = static_cast<uint32_t>(pos), bs = static_cast<uint32_t>(block_size);   // pos < 2^30
+        const int64_t blk = block_table[static_cast<int64_t>(b) * max_blocks + p / bs];
+        return (blk * h_kv + g) * block_size + p % bs;
     }
     __device__ __forceinline__ int64_t row_offset(int b, int g, int64_t pos) const {
         if (block_size == 0) {
             return ((static_cast<int64_t>(b) * h_kv + g) * capacity + pos) * row_bytes;
         }
-        int64_t blk = block_table[static_cast<int64_t>(b) * max_blocks + pos / block_size];
-        return ((blk * h_kv + g) * block_size + pos % block_size) * static_cast<int64_t>(row_bytes);
+        const uint32_t p = static_cast<uint32_t>(pos), bs = static_cast<uint32_t>(block_size);   // pos < 2^30
+        const int64_t blk = block_table[static_cast<int64_t>(b) * max_blocks + p / bs];
+        return ((blk * h_kv + g) * block_size + p % bs) * static_cast<int64_t>(row_bytes);
     }
 };
 

@@ -10,6 +10,10 @@
 // bf16); 1/|k_j| is common to every query so it is applied after the max.
 #include "launch.h"
 
+#ifndef KVSEL_ROWS16_GROUPS
+#define KVSEL_ROWS16_GROUPS 4   // 16-key groups per wave of the one-query scan
+#endif
+
 namespace kvsel {
 
 // ----------------------------------------------------------------------------- prefill scan (MFMA 32x32x16)
@@ -180,14 +184,13 @@ __global__ __launch_bounds__(256, 2) void scan_mfma_kernel(const uint16_t* __res
 // With a single query per head (decode, or N_q = 1) the G <= 16 query heads of
 // a KV head form the 16 rows of one MFMA tile; keys stream through registers
 // straight from HBM (this scan is bandwidth-bound: 4 useful rows per key).
-template <int D>
+template <int D, int GROUPS>
 __global__ __launch_bounds__(256) void scan_rows16_kernel(const uint16_t* __restrict__ qsel,
                                                          const float* __restrict__ rq, CacheView cv,
                                                          const int64_t* __restrict__ prior_len, int64_t budget,
                                                          int h_kv, int G, int tiles, float* __restrict__ S,
                                                          int64_t s_stride) {
     constexpr int KS = D / 32;          // k-steps of 32
-    constexpr int GROUPS = 4;           // 16-key groups per wave
     constexpr int KEYS = 4 * GROUPS * 16;
     const int slot = xcd_slot(blockIdx.x, gridDim.x);
     const int bg = slot / tiles, tile = slot % tiles;
@@ -313,10 +316,11 @@ hipError_t launch_scan(const SelShape& s, const void* qsel, const float* rq, con
                        const int64_t* prior_len, float* S, int64_t s_stride, hipStream_t st) {
     const int bgs = s.batch * s.h_kv;
     if (s.esz == 2 && s.nq_pad == 1 && !s.qsplit) {   // one query per head, G <= 16
-        const int tiles = static_cast<int>((s.t_max + 255) / 256);
+        constexpr int GR = KVSEL_ROWS16_GROUPS;
+        const int tiles = static_cast<int>((s.t_max + 64 * GR - 1) / (64 * GR));
         dim3 grid(bgs * tiles), block(256);
-        if (s.d == 128) hipLaunchKernelGGL((scan_rows16_kernel<128>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride);
-        else hipLaunchKernelGGL((scan_rows16_kernel<64>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride);
+        if (s.d == 128) hipLaunchKernelGGL((scan_rows16_kernel<128, GR>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride);
+        else hipLaunchKernelGGL((scan_rows16_kernel<64, GR>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride);
     } else if (s.esz == 2) {
         constexpr int NB = 2;
         const int tiles = static_cast<int>((s.t_max + 4 * NB * 32 - 1) / (4 * NB * 32));
