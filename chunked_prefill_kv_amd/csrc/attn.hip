@@ -136,11 +136,12 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
 
     const uint16_t* kb = kall + static_cast<int64_t>(bg) * nk_pad * D;
     const uint16_t* vb = vall + static_cast<int64_t>(bg) * D * nk_pad;
-    // Staging with a full tile of latency for every load: V(t+1) is fetched at
-    // the start of tile t and written to LDS at its end; K(t+1), fetched in the
-    // middle of tile t-1, is written after t's S MFMAs and K(t+2) is fetched
-    // then.  Buffer (t+1)&1 was last read in tile t-1 and buffer t&1 (K(t+2))
-    // in tile t, each closed by a barrier before the write.
+    // Staging with a full tile of latency for every load (t counts tiles in
+    // the order this workgroup reads them): V(t+1) is fetched at the start of
+    // tile t and written to LDS at its end; K(t+1), fetched in the middle of
+    // tile t-1, is written after t's S MFMAs and K(t+2) is fetched then.
+    // Buffer (t+1)&1 was last read in tile t-1 and buffer t&1 (K(t+2)) in
+    // tile t, each closed by a barrier before the write.
     u32x4 rk[PK], rv[PV];
     // Per-thread byte offsets inside a tile, fixed for the whole loop: a load
     // is a buffer load with this lane offset and the tile's uniform offset
@@ -160,9 +161,12 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
     // end return 0); the tile offset is the uniform soffset operand
     const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kb), 0, nk_pad * D * 2, kBufferFormat);
     const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vb), 0, nk_pad * D * 2, kBufferFormat);
+    // the tile index is the same in every lane; readfirstlane hands it to the
+    // scalar offset operand directly (no per-lane waterfall over its values)
     auto fetch_k = [&](int t) {
+        const int so = __builtin_amdgcn_readfirstlane(t * KT * D * 2);
 #pragma unroll
-        for (int i = 0; i < PK; ++i) rk[i] = __builtin_amdgcn_raw_buffer_load_b128(rsk, koff[i], t * KT * D * 2, 0);
+        for (int i = 0; i < PK; ++i) rk[i] = __builtin_amdgcn_raw_buffer_load_b128(rsk, koff[i], so, 0);
     };
     // Gathering: slot s < n_s is cache row rowidx[s], then the chunk's rows
     // (coded -1 - chunk row); slots past the list read the chunk's last row
@@ -197,8 +201,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
         }
     };
     auto fetch_v = [&](int t) {
+        const int so = __builtin_amdgcn_readfirstlane(t * KT * 2);
 #pragma unroll
-        for (int i = 0; i < PV; ++i) rv[i] = __builtin_amdgcn_raw_buffer_load_b128(rsv, voff[i], t * KT * 2, 0);
+        for (int i = 0; i < PV; ++i) rv[i] = __builtin_amdgcn_raw_buffer_load_b128(rsv, voff[i], so, 0);
     };
     auto stash_v = [&](int buf) {
 #pragma unroll
@@ -409,6 +414,17 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
     // latency.
     const int t_last = max(t_beg + ntiles - 1, 0);
     auto tc = [&](int t) { return min(t, t_last); };
+    // Packed path: the row blocks of one KV head (all on one XCD) start their
+    // tile sequence at evenly spaced tiles and wrap around, so at any moment
+    // they read different tiles rather than all requesting the same lines from
+    // the L2 at once (the softmax is order-independent; the per-tile mask
+    // tests take the tile's own position).  tix(u) is the u-th tile read;
+    // past the last one it repeats the last one (always in bounds).
+    const int rot = ntiles > 0 ? (rblk * ntiles) / row_blocks : 0;
+    auto tix = [&](int uu) {
+        const int v = min(uu, max(ntiles - 1, 0)) + rot;
+        return t_beg + (v >= ntiles ? v - ntiles : v);
+    };
     if constexpr (GATHER) {
         static_assert(PK == PV, "K and V rows are fetched together");
         rows_of(tc(t_beg), R1);
@@ -423,16 +439,16 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
         rows_of(tc(t_beg + 2), R2);
     } else {
         if (ntiles > 0) {
-            fetch_k(t_beg);
-            fetch_v(t_beg);
+            fetch_k(tix(0));
+            fetch_v(tix(0));
             stash_k(0);
             stash_v(0);
         }
-        fetch_k(tc(t_beg + 1));
+        fetch_k(tix(1));
     }
     __syncthreads();
     for (int u = 0; u < ntiles; ++u) {           // u: tile within this workgroup's range
-        const int t = t_beg + u;
+        const int t = GATHER ? t_beg + u : tix(u);
         const int buf = u & 1;
         if constexpr (GATHER) {
             gfetch(R1, true, rv);                // V(t+1)
@@ -440,12 +456,12 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
             for (int i = 0; i < PK; ++i) R1[i] = R2[i];
             rows_of(tc(t + 3), R2);
         } else {
-            fetch_v(tc(t + 1));
+            fetch_v(tix(u + 1));
         }
         auto mid = [&] {
             if (u + 1 < ntiles) stash_k(buf ^ 1);
             if constexpr (GATHER) gfetch(R1, false, rk);   // K(t+2)
-            else fetch_k(tc(t + 2));
+            else fetch_k(tix(u + 2));
         };
         const int s0 = t * KT;
         if (wave_active && s0 <= n_s + w_tmax) {
