@@ -82,12 +82,17 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
     constexpr int LDK = D + 8;
     constexpr int LDV = VR ? D + 16 : KT + 8;   // V tile row: [key][d] (pitch spreads a transpose
                                                  // load over 4 bank groups) or [d][key]
+    constexpr int KSZ = KT * LDK;               // stage sizes in elements
+    constexpr int VSZ = VR ? KT * LDV : D * LDV;
     constexpr int NT = 64 * WAVES;          // threads per workgroup
     constexpr int ROWS = 32 * WAVES;        // query rows per workgroup
     constexpr int PK = KT * D / 8 / NT;     // 16-byte K pieces per thread per tile
     constexpr int PV = D * KT / 8 / NT;     // 16-byte V^T pieces per thread per tile
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][VR ? KT * LDV : D * LDV];
+    // the two stages as two arrays (a stage is picked by a select)
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds0[KSZ], k_lds1[KSZ];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds0[VSZ], v_lds1[VSZ];
+    auto kl = [&](int buf) -> uint16_t* { return buf ? k_lds1 : k_lds0; };
+    auto vl = [&](int buf) -> uint16_t* { return buf ? v_lds1 : v_lds0; };
 
     // slot -> (KV head, row block, key split); later row blocks (more keys) first
     const int slot = xcd_slot(blockIdx.x, gridDim.x);
@@ -197,7 +202,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
         for (int i = 0; i < PK; ++i) {
             const int p = tid + NT * i;
             const int r = p / (D / 8), c = p % (D / 8);
-            *reinterpret_cast<u32x4*>(&k_lds[buf][r * LDK + c * 8]) = rk[i];
+            *reinterpret_cast<u32x4*>(&kl(buf)[r * LDK + c * 8]) = rk[i];
         }
     };
     auto fetch_v = [&](int t) {
@@ -211,10 +216,10 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
             const int p = tid + NT * i;
             if (VR) {
                 const int r = p / (D / 8), c = p % (D / 8);
-                *reinterpret_cast<u32x4*>(&v_lds[buf][r * LDV + c * 8]) = rv[i];
+                *reinterpret_cast<u32x4*>(&vl(buf)[r * LDV + c * 8]) = rv[i];
             } else {
                 const int d = p / (KT / 8), j = p % (KT / 8);
-                *reinterpret_cast<u32x4*>(&v_lds[buf][d * LDV + j * 8]) = rv[i];
+                *reinterpret_cast<u32x4*>(&vl(buf)[d * LDV + j * 8]) = rv[i];
             }
         }
     };
@@ -232,12 +237,12 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
             const int j = lane & 15;
             const int row = k0 + 8 * half + (j >> 2);
             const int colv = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
-            const v4s x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)&v_lds[buf][row * LDV + colv]);
-            const v4s x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)&v_lds[buf][(row + 4) * LDV + colv]);
+            const v4s x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)&vl(buf)[row * LDV + colv]);
+            const v4s x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)&vl(buf)[(row + 4) * LDV + colv]);
             const v8s x = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
             return __builtin_bit_cast(bf16x8, x);
         }
-        return *reinterpret_cast<const bf16x8*>(&v_lds[buf][(32 * db + col) * LDV + k0 + 8 * half]);
+        return *reinterpret_cast<const bf16x8*>(&vl(buf)[(32 * db + col) * LDV + k0 + 8 * half]);
     };
 
     f32x16 o[DB];
@@ -245,6 +250,10 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
     for (int db = 0; db < DB; ++db) o[db] = f32x16{};
     float m = -INFINITY, l = 0.0f;
     const int krow = sigma(col);
+    // K fragment of the S MFMA: key 32*kb2 + krow, elements 16*ks + 8*half .. +7
+    auto kfrag = [&](int buf, int kb2, int ks) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8*>(&kl(buf)[(32 * kb2 + krow) * LDK + 16 * ks + 8 * half]);
+    };
     const int lim = n_s + tok;                  // last visible slot of this lane's query
 
     // One KT-key tile: S^T, online softmax, O^T += V^T P^T.  MASK applies the
@@ -261,7 +270,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
             sacc[kb2] = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[buf][(32 * kb2 + krow) * LDK + 16 * ks + 8 * half]);
+                const bf16x8 a = kfrag(buf, kb2, ks);
                 sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb2], 0, 0, 0);
             }
         }
@@ -336,7 +345,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
             sacc[kb2] = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[buf][(32 * kb2 + krow) * LDK + 16 * ks + 8 * half]);
+                const bf16x8 a = kfrag(buf, kb2, ks);
                 sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb2], 0, 0, 0);
             }
         }
@@ -447,9 +456,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
         fetch_k(tix(1));
     }
     __syncthreads();
-    for (int u = 0; u < ntiles; ++u) {           // u: tile within this workgroup's range
+    // one tile: u counts tiles within this workgroup's range, buf is its stage
+    auto step = [&](const int u, const int buf) {
         const int t = GATHER ? t_beg + u : tix(u);
-        const int buf = u & 1;
         if constexpr (GATHER) {
             gfetch(R1, true, rv);                // V(t+1)
 #pragma unroll
@@ -477,7 +486,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
         }
         if (u + 1 < ntiles) stash_v(buf ^ 1);
         __syncthreads();
-    }
+    };
+    for (int u = 0; u < ntiles; ++u) step(u, u & 1);
 
     l = half_sum(l);
     if (!rvalid) return;
