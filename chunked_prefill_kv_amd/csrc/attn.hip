@@ -62,6 +62,9 @@ __device__ __forceinline__ int sigma(int m) {
 #ifndef KVSEL_ATTN_GATHER
 #define KVSEL_ATTN_GATHER 1               // gathering attention for single-row-block KV heads
 #endif
+#ifndef KVSEL_ATTN_PP
+#define KVSEL_ATTN_PP 1                   // packed path: ping-pong kernel (8 waves, 256 rows)
+#endif
 
 //
 // GATHER: the key list is read from its sources (kept cache rows through idx,
@@ -528,6 +531,302 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
         }
 }
 
+// ----------------------------------------------------------------------------- ping-pong MFMA kernel
+//
+// Packed path, 8 waves x 32 query rows.  Waves w and w + 4 share a SIMD; the
+// two groups of four (A = waves 0-3, B = waves 4-7) run the same tile loop
+// half a tile apart, so that on every SIMD one wave issues MFMAs while the
+// other computes a softmax.  For tile t a wave runs
+//   M(t): O += P(t-1) V(t-1) (if t >= 1), then S(t) = K(t) Q^T (if t < n)
+//   X(t): online softmax of S(t) -> P(t), running max and sum, rescale of O
+// each followed by a workgroup barrier; group B passes one barrier before
+// the loop and group A one after it, so M(t) of one group runs beside X(t-1)
+// (or X(t)) of the other and every wave passes the same 2n+4 barriers.  The
+// rescale of O by X(t) comes after M(t) has added P(t-1) V(t-1) and before
+// M(t+1) adds P(t) V(t), the order of the sequential recurrence.
+// Staging: each thread owns pieces tid and tid + 512 of every K and V^T tile
+// (16 bytes each) and writes one piece in each half of its loop, 2 barriers
+// after fetching it.  Between barriers 2u and 2u+1 (counted from the first
+// loop barrier of group A) the workgroup writes half of K(u+1) and of V(u),
+// the other halves in the next interval, while K(u) and V(u-1) are read.
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(512, 1) void attn_pp_kernel(const uint16_t* __restrict__ q,
+                                                       const uint16_t* __restrict__ kall,
+                                                       const uint16_t* __restrict__ vall,
+                                                       const int32_t* __restrict__ nsel, int nk_pad, int C, int G,
+                                                       int h_kv, int row_blocks, float cl2, void* __restrict__ out,
+                                                       int ksplit, float* __restrict__ part) {
+    constexpr int KT = 64, NT = 512, ROWS = 256;
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    constexpr int NKB = KT / 32;
+    constexpr int LDK = D + 8;
+    constexpr int LDV = KT + 8;
+    constexpr int PK = KT * D / 8 / NT;     // 16-byte pieces per thread per K (or V^T) tile
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds0[KT * LDK], k_lds1[KT * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds0[D * LDV], v_lds1[D * LDV];
+    auto kl = [&](int buf) -> uint16_t* { return buf ? k_lds1 : k_lds0; };
+    auto vl = [&](int buf) -> uint16_t* { return buf ? v_lds1 : v_lds0; };
+
+    const int slot = xcd_slot(blockIdx.x, gridDim.x);
+    const int bg = slot / (row_blocks * ksplit);
+    const int rem = slot % (row_blocks * ksplit);
+    const int rblk = row_blocks - 1 - rem / ksplit;
+    const int ksp = rem % ksplit;
+    const int b = bg / h_kv, g = bg % h_kv;
+    const int nrows = G * C;
+    const int n_s = nsel[b];
+    const int row_wg0 = rblk * ROWS;
+    const int wg_tmax = min(row_wg0 + ROWS - 1, nrows - 1) / G;
+    const int ntiles_all = (n_s + wg_tmax + 1 + KT - 1) / KT;
+    const int per = (ntiles_all + ksplit - 1) / ksplit;
+    const int t_beg = min(ntiles_all, ksp * per);
+    const int ntiles = min(ntiles_all, t_beg + per) - t_beg;
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);   // 0: group A, 1: group B (half a tile later)
+    const int half = lane >> 5, col = lane & 31;
+    const int wrow0 = row_wg0 + wave * 32;
+    const bool wave_active = wrow0 < nrows;
+    const int w_tmin = min(wrow0, nrows - 1) / G;
+    const int w_tmax = min(wrow0 + 31, nrows - 1) / G;
+    const int qrow = wrow0 + col;
+    const bool rvalid = qrow < nrows;
+    const int tok = rvalid ? qrow / G : 0;
+    const int hh = rvalid ? qrow % G : 0;
+    const int64_t qoff = ((static_cast<int64_t>(b) * h_kv * G + g * G + hh) * C + tok) * D;
+
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (rvalid) raw = *reinterpret_cast<const u32x4*>(q + qoff + 16 * ks + 8 * half);
+        qf[ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+
+    const uint16_t* kb = kall + static_cast<int64_t>(bg) * nk_pad * D;
+    const uint16_t* vb = vall + static_cast<int64_t>(bg) * D * nk_pad;
+    // piece h of this thread is tile piece tid + NT*h (h = 0, 1); a K piece is
+    // row p / (D/8), chunk p % (D/8), a V^T piece row p / (KT/8), chunk p % (KT/8)
+    static_assert(PK == 2, "two 16-byte pieces per thread per tile (d = 128)");
+    u32x4 rk[2], rv[2];
+    uint32_t koff[2], voff[2], kst[2], vst[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int p = tid + NT * h;
+        koff[h] = static_cast<uint32_t>(((p / (D / 8)) * D + (p % (D / 8)) * 8) * 2);
+        voff[h] = static_cast<uint32_t>(((p / (KT / 8)) * nk_pad + (p % (KT / 8)) * 8) * 2);
+        kst[h] = static_cast<uint32_t>((p / (D / 8)) * LDK + (p % (D / 8)) * 8);
+        vst[h] = static_cast<uint32_t>((p / (KT / 8)) * LDV + (p % (KT / 8)) * 8);
+    }
+    const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kb), 0, nk_pad * D * 2, kBufferFormat);
+    const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vb), 0, nk_pad * D * 2, kBufferFormat);
+    // piece h of K tile tk and V^T tile tv into registers / from registers to stages
+    auto fetch = [&](int h, int tk, int tv) {
+        rk[h] = __builtin_amdgcn_raw_buffer_load_b128(rsk, koff[h], __builtin_amdgcn_readfirstlane(tk * KT * D * 2), 0);
+        rv[h] = __builtin_amdgcn_raw_buffer_load_b128(rsv, voff[h], __builtin_amdgcn_readfirstlane(tv * KT * 2), 0);
+    };
+    auto stash = [&](int h, int kbuf, int vbuf) {
+        *reinterpret_cast<u32x4*>(kl(kbuf) + kst[h]) = rk[h];
+        *reinterpret_cast<u32x4*>(vl(vbuf) + vst[h]) = rv[h];
+    };
+    // tiles in a rotated order per row block (as in attn_mfma_kernel); past
+    // the last tile the index repeats the last one (always in bounds)
+    const int rot = ntiles > 0 ? (rblk * ntiles) / row_blocks : 0;
+    auto tix = [&](int uu) {
+        const int v = min(uu, max(ntiles - 1, 0)) + rot;
+        return t_beg + (v >= ntiles ? v - ntiles : v);
+    };
+
+    f32x16 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+    float m = -INFINITY, l = 0.0f;
+    const int krow = sigma(col);
+    const int lim = n_s + tok;
+    f32x16 sacc[NKB];                       // S(t), from M(t) to X(t)
+    bf16x8 pf[NKB][2];                      // P(t), from X(t) to M(t+1)
+    auto live = [&](int t) { return t < ntiles && wave_active && tix(t) * KT <= n_s + w_tmax; };
+
+    // M(t) as four groups of 8 MFMAs (P.V for each 32-key block, then S for
+    // each); a group's 8 fragments are read from LDS before the previous
+    // group's MFMAs are issued, so the reads' latency hides behind them
+    auto rd_v = [&](int buf, int kb2, bf16x8 (&f)[8]) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int k16 = 0; k16 < 2; ++k16)
+                f[2 * db + k16] = *reinterpret_cast<const bf16x8*>(
+                    &vl(buf)[(32 * db + col) * LDV + 32 * kb2 + 16 * k16 + 8 * half]);
+    };
+    auto rd_k = [&](int buf, int kb2, bf16x8 (&f)[8]) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            f[ks] = *reinterpret_cast<const bf16x8*>(&kl(buf)[(32 * kb2 + krow) * LDK + 16 * ks + 8 * half]);
+    };
+    auto mm_v = [&](int kb2, const bf16x8 (&f)[8]) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int k16 = 0; k16 < 2; ++k16)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[2 * db + k16], pf[kb2][k16], o[db], 0, 0, 0);
+    };
+    auto mm_k = [&](int kb2, const bf16x8 (&f)[8]) {
+        sacc[kb2] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks], qf[ks], sacc[kb2], 0, 0, 0);
+    };
+    static_assert(2 * DB == 8 && KS == 8, "8 fragments per group (d = 128)");
+    auto phase_m = [&](int t) {
+        KVSEL_SETPRIO(1);
+        const bool pv = t >= 1 && live(t - 1), sk = live(t);   // O += P(t-1) V(t-1); S(t)^T = K(t) Q^T
+        const int vb_ = (t - 1) & 1, kb_ = t & 1;
+        bf16x8 fa[8], fb[8];
+        // (sched_barrier: the scheduler would otherwise sink each read to just
+        // before its MFMA and expose the LDS latency)
+        if (pv && sk) {
+            rd_v(vb_, 0, fa);
+            rd_v(vb_, 1, fb);
+            __builtin_amdgcn_sched_barrier(0);
+            mm_v(0, fa);
+            rd_k(kb_, 0, fa);
+            __builtin_amdgcn_sched_barrier(0);
+            mm_v(1, fb);
+            rd_k(kb_, 1, fb);
+            __builtin_amdgcn_sched_barrier(0);
+            mm_k(0, fa);
+            mm_k(1, fb);
+        } else if (pv) {
+            rd_v(vb_, 0, fa);
+            rd_v(vb_, 1, fb);
+            __builtin_amdgcn_sched_barrier(0);
+            mm_v(0, fa);
+            mm_v(1, fb);
+        } else if (sk) {
+            rd_k(kb_, 0, fa);
+            rd_k(kb_, 1, fb);
+            __builtin_amdgcn_sched_barrier(0);
+            mm_k(0, fa);
+            mm_k(1, fb);
+        }
+        KVSEL_SETPRIO(0);
+    };
+    // X(t): the running max moves only when it grows by more than 2^8 (log2
+    // units), as in attn_mfma_kernel
+    auto phase_x = [&](int t) {
+        if (!live(t)) return;
+        const int s0 = tix(t) * KT;
+        if (s0 + KT > n_s + w_tmin + 1) {    // causal limit reaches into this tile
+#pragma unroll
+            for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int sl = s0 + 32 * kb2 + 16 * (r >> 3) + 8 * half + (r & 7);
+                    if (sl > lim) sacc[kb2][r] = -INFINITY;
+                }
+        }
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb2][r]);
+        mt = half_max(mt);
+        const float m_new = fmaxf(m, mt);
+        if (__ballot((m_new - m) * cl2 > 8.0f) != 0ull) {
+            const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m - m_new) * cl2);
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            m = m_new;
+        }
+        const float mc = m == -INFINITY ? 0.0f : m * cl2;
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+            for (int k16 = 0; k16 < 2; ++k16) {
+                u32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e], cl2, -mc));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e + 1], cl2, -mc));
+                    l += p0 + p1;
+                    w[e] = pack_bf16x2(p0, p1);
+                }
+                pf[kb2][k16] = __builtin_bit_cast(bf16x8, w);
+            }
+    };
+
+    // prologue: K(0) staged whole; registers hold K(1) and V(0) (both pieces)
+    if (ntiles > 0) {
+        fetch(0, tix(0), tix(0));
+        fetch(1, tix(0), tix(0));
+        stash(0, 0, 0);
+        stash(1, 0, 0);                      // V(0) also lands in stage 0 here (rewritten below)
+        fetch(0, tix(1), tix(0));
+        fetch(1, tix(1), tix(0));
+    }
+    __syncthreads();
+    if (ntiles > 0 && grp == 1) {            // group B: the second half of the interval before the loop
+        stash(1, 1, 0);                      // K(1), V(0) piece 1
+        fetch(1, tix(2), tix(1));
+        __syncthreads();
+    }
+    const int nloop = ntiles > 0 ? ntiles + 1 : 0;
+    for (int t = 0; t < nloop; ++t) {
+        stash(0, (t + 1) & 1, t & 1);        // K(t+1), V(t) piece 0
+        fetch(0, tix(t + 2), tix(t + 1));
+        phase_m(t);
+        __syncthreads();
+        stash(1, (t + 1 + grp) & 1, (t + grp) & 1);   // group A: K(t+1), V(t); B: K(t+2), V(t+1)
+        fetch(1, tix(t + 2 + grp), tix(t + 1 + grp));
+        phase_x(t);
+        __syncthreads();
+    }
+    if (ntiles > 0 && grp == 0) __syncthreads();   // group A: the interval after the loop
+
+    l = half_sum(l);
+    if (!rvalid) return;
+    if (ksplit > 1) {
+        const int64_t rows_total = static_cast<int64_t>(gridDim.x / (row_blocks * ksplit)) * nrows;
+        float* po = part + static_cast<int64_t>(ksp) * rows_total * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int d0 = 32 * db + 8 * a4 + 4 * half;
+                *reinterpret_cast<f32x4*>(po + qoff + d0) =
+                    f32x4{o[db][4 * a4 + 0], o[db][4 * a4 + 1], o[db][4 * a4 + 2], o[db][4 * a4 + 3]};
+            }
+        if (half == 0) {
+            float* pml = part + static_cast<int64_t>(ksplit) * rows_total * D + (static_cast<int64_t>(ksp) * rows_total + qoff / D) * 2;
+            pml[0] = m;
+            pml[1] = l;
+        }
+        return;
+    }
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+            const int d0 = 32 * db + 8 * a4 + 4 * half;
+            const float v0 = o[db][4 * a4 + 0] * inv, v1 = o[db][4 * a4 + 1] * inv;
+            const float v2 = o[db][4 * a4 + 2] * inv, v3 = o[db][4 * a4 + 3] * inv;
+            if (OUT_F32) {
+                *reinterpret_cast<f32x4*>(static_cast<float*>(out) + qoff + d0) = f32x4{v0, v1, v2, v3};
+            } else {
+                uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + qoff + d0);
+                dst[0] = pack_bf16x2(v0, v1);
+                dst[1] = pack_bf16x2(v2, v3);
+            }
+        }
+}
+
 // ----------------------------------------------------------------------------- split merge
 //
 // out = sum_s w_s O_s / sum_s w_s l_s with w_s = exp2((m_s - max_s m_s) * cl2):
@@ -637,15 +936,28 @@ __global__ __launch_bounds__(128) void attn_valu_kernel(const float* __restrict_
 // ----------------------------------------------------------------------------- launcher
 
 bool attn_use_gather(const SelShape& s) { return KVSEL_ATTN_GATHER && s.esz == 2 && s.G * s.C <= 128; }
+// Ping-pong kernel: packed bf16 path with d = 128 (two staged pieces per
+// thread), where its 256-row grid either splits keys (fewer workgroups than
+// CUs) or holds two or more workgroups per CU.  In between (one round of one
+// workgroup per CU) the 4-wave kernel measured faster (2% on 8 KV heads x 32
+// row blocks); with splits and with several rounds the ping-pong kernel was
+// 1.7-3% faster.
+static bool attn_use_pp(const SelShape& s) {
+    if (!(KVSEL_ATTN_PP && s.esz == 2 && s.d == 128 && !attn_use_gather(s))) return false;
+    const int64_t wgs = int64_t(s.batch) * s.h_kv * ((s.G * s.C + 255) / 256);
+    return wgs < 256 || wgs >= 512;
+}
 
 int attn_ksplit(const SelShape& s) {
     if (s.esz != 2) return 1;
     // gathering workgroups wait on dependent loads (index, block table, row):
     // four shorter key ranges per row block keep more of them in flight
     if (attn_use_gather(s)) return 4;
-    const int64_t wgs = int64_t(s.batch) * s.h_kv * ((s.G * s.C + 127) / 128);
+    // at least two 4-wave workgroups, or one 8-wave ping-pong workgroup, per CU
+    const int rows = attn_use_pp(s) ? 256 : 128, target = attn_use_pp(s) ? 256 : 512;
+    const int64_t wgs = int64_t(s.batch) * s.h_kv * ((s.G * s.C + rows - 1) / rows);
     int k = 1;
-    while (k < 4 && wgs * k < 512) k *= 2;            // at least two workgroups per CU
+    while (k < 4 && wgs * k < target) k *= 2;
     return k;
 }
 
@@ -664,18 +976,22 @@ hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const
         // 8-wave workgroups share one staged copy of every K/V tile; fall back to
         // 4 waves when that would leave fewer than 256 workgroups
         const int rb8 = (s.G * s.C + 255) / 256, rb4 = (s.G * s.C + 127) / 128;
-        const bool w8 = !gather && KVSEL_ATTN_WAVES == 8 && bgs * rb8 >= 256;
-        const int row_blocks = w8 ? rb8 : rb4;
+        const bool pp = !gather && attn_use_pp(s);
+        const bool w8 = !gather && !pp && KVSEL_ATTN_WAVES == 8 && bgs * rb8 >= 256;
+        const int row_blocks = (w8 || pp) ? rb8 : rb4;
         const int ksplit = w8 ? 1 : attn_ksplit(s);
-        dim3 grid(bgs * row_blocks * ksplit), block(w8 ? 512 : 256);
+        dim3 grid(bgs * row_blocks * ksplit), block((w8 || pp) ? 512 : 256);
         const float cl2 = scale * 1.4426950408889634f;
         const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)kall, *vv = (const uint16_t*)vall;
         const AttnGather ga = gather ? *gather : AttnGather{};
 #define KVSEL_ATTN(D, F32, W) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, KVSEL_ATTN_KT, W, false>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part, ga)
 #define KVSEL_ATTN_G(D, F32) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, KVSEL_ATTN_KT, 4, true>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part, ga)
+#define KVSEL_ATTN_PPK(D, F32) hipLaunchKernelGGL((attn_pp_kernel<D, F32>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part)
         if (gather) {
             if (s.d == 128) { if (out_f32) KVSEL_ATTN_G(128, true); else KVSEL_ATTN_G(128, false); }
             else { if (out_f32) KVSEL_ATTN_G(64, true); else KVSEL_ATTN_G(64, false); }
+        } else if (pp) {
+            if (out_f32) KVSEL_ATTN_PPK(128, true); else KVSEL_ATTN_PPK(128, false);
         } else if (s.d == 128) {
             if (w8) { if (out_f32) KVSEL_ATTN(128, true, 8); else KVSEL_ATTN(128, false, 8); }
             else { if (out_f32) KVSEL_ATTN(128, true, 4); else KVSEL_ATTN(128, false, 4); }
@@ -685,6 +1001,7 @@ hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const
         }
 #undef KVSEL_ATTN
 #undef KVSEL_ATTN_G
+#undef KVSEL_ATTN_PPK
         if (ksplit > 1) {
             const int64_t rows = int64_t(s.batch) * s.h_q * s.C;
             const dim3 mg(static_cast<unsigned>((rows * (s.d / 4) + 255) / 256));
