@@ -24,6 +24,12 @@ struct SelShape {
 // Choose how many query-head groups the MFMA scan splits a KV head into: a
 // power of two dividing G (at most 8), the smallest that gives >= 512
 // workgroups for the largest prior length.
+#ifndef KVSEL_SCAN_NB
+#define KVSEL_SCAN_NB 3
+#endif
+constexpr int kScanNB = KVSEL_SCAN_NB;   // 32-key blocks per wave of the prefill scan (4 waves)
+// (counted in 256-key tiles whatever kScanNB is: every split adds a pass of
+// the top-B over the scores, so the split count is not raised with the tile)
 inline int scan_splits(int batch, int h_kv, int G, int64_t t_max) {
     const int64_t tiles = (t_max + 255) / 256;
     int ns = 1;

@@ -322,15 +322,17 @@ hipError_t launch_scan(const SelShape& s, const void* qsel, const float* rq, con
         if (s.d == 128) hipLaunchKernelGGL((scan_rows16_kernel<128, GR>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride);
         else hipLaunchKernelGGL((scan_rows16_kernel<64, GR>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride);
     } else if (s.esz == 2) {
-        constexpr int NB = 2;
-        const int tiles = static_cast<int>((s.t_max + 4 * NB * 32 - 1) / (4 * NB * 32));
+        // 32-key blocks per wave: kScanNB for bf16 query rows; 2 for [hi | lo]
+        // pairs (twice the query fragments per key block)
+        const int nb = s.qsplit ? 2 : kScanNB;
+        const int tiles = static_cast<int>((s.t_max + 4 * nb * 32 - 1) / (4 * nb * 32));
         dim3 grid(bgs * tiles * s.nsplit), block(256);
         const int64_t split_stride = int64_t(bgs) * s_stride;
-#define KVSEL_SCAN(D, QK) hipLaunchKernelGGL((scan_mfma_kernel<D, NB, QK>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, s.nsplit, S, s_stride, split_stride)
+#define KVSEL_SCAN(D, NB, QK) hipLaunchKernelGGL((scan_mfma_kernel<D, NB, QK>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, s.nsplit, S, s_stride, split_stride)
         if (s.qsplit) {
-            if (s.d == 128) KVSEL_SCAN(128, 2); else KVSEL_SCAN(64, 2);
+            if (s.d == 128) KVSEL_SCAN(128, 2, 2); else KVSEL_SCAN(64, 2, 2);
         } else {
-            if (s.d == 128) KVSEL_SCAN(128, 1); else KVSEL_SCAN(64, 1);
+            if (s.d == 128) KVSEL_SCAN(128, kScanNB, 1); else KVSEL_SCAN(64, kScanNB, 1);
         }
 #undef KVSEL_SCAN
     } else {
