@@ -138,25 +138,37 @@ __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
     const int bstar = static_cast<int>(s_bin);
     const uint32_t need = s_need;                 // keys kept from the boundary bin
     const float* c = a.comb + static_cast<int64_t>(p) * a.s_stride;
-    // one pass: keys above the boundary bin are counted per segment, boundary keys collected
+    // one pass: keys above the boundary bin are counted per segment, boundary
+    // keys collected.  Wave w takes keys [base0 + 512 w, +512) in 8 steps of
+    // 64 (one segment: the count stays in a register, one LDS atomic per wave
+    // and pass), boundary keys are appended with one atomic per wave and step.
+    const uint64_t lt = (1ull << lane) - 1ull;
     for (int base0 = 0; base0 < T; base0 += 8 * 1024) {
+        const int wbase = base0 + wave * 512;
         float v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {                  // 8 loads in flight per thread
-            const int j = base0 + i * 1024 + tid;
+            const int j = wbase + i * kWave + lane;
             v[i] = j < T ? c[j] : -2.0f;
         }
+        uint32_t ngt = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int base = base0 + i * 1024, j = base + tid;
+            const int j = wbase + i * kWave + lane;
             const int bn = j < T ? value_bin(v[i]) : -1;
-            const uint64_t bgt = __ballot(bn > bstar);
-            if (lane == 0 && bgt) atomicAdd(&sgt[(base + wave * kWave) / kSeg], static_cast<uint32_t>(__popcll(bgt)));
-            if (bn == bstar) {
-                const uint32_t pos = atomicAdd(&s_cnt, 1u);
-                if (pos < kCap) { ck[pos] = order_key(v[i]); cj[pos] = j; }
+            ngt += static_cast<uint32_t>(__popcll(__ballot(bn > bstar)));
+            const uint64_t beq = __ballot(bn == bstar);
+            if (beq) {
+                uint32_t first = 0;
+                if (lane == 0) first = atomicAdd(&s_cnt, static_cast<uint32_t>(__popcll(beq)));
+                first = __shfl(first, 0, kWave);
+                if (bn == bstar) {
+                    const uint32_t pos = first + static_cast<uint32_t>(__popcll(beq & lt));
+                    if (pos < kCap) { ck[pos] = order_key(v[i]); cj[pos] = j; }
+                }
             }
         }
+        if (lane == 0 && ngt) atomicAdd(&sgt[wbase / kSeg], ngt);
     }
     __syncthreads();
     const uint32_t cnt = s_cnt;
