@@ -53,12 +53,6 @@ __device__ __forceinline__ int sigma(int m) {
 #define KVSEL_ATTN_PRIO 1
 #endif
 #define KVSEL_SETPRIO(p) do { if (KVSEL_ATTN_PRIO) __builtin_amdgcn_s_setprio(p); } while (0)
-#ifndef KVSEL_ATTN_WAVES
-#define KVSEL_ATTN_WAVES 4
-#endif
-#ifndef KVSEL_ATTN_PIPE
-#define KVSEL_ATTN_PIPE 0
-#endif
 #ifndef KVSEL_ATTN_GATHER
 #define KVSEL_ATTN_GATHER 1               // gathering attention for single-row-block KV heads
 #endif
@@ -338,87 +332,6 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
         }
     };
 
-    // Variant: one max/rescale per tile, then a branch-free region in which the
-    // P.V MFMAs of block kb interleave with the exponentials of block kb+1.
-    auto tile_pipe = [&](const int buf, const int s0, auto mask_tag, auto&& mid) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        f32x16 sacc[NKB];
-#pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2) {
-            sacc[kb2] = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = kfrag(buf, kb2, ks);
-                sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb2], 0, 0, 0);
-            }
-        }
-        mid();
-        if (MASK) {
-#pragma unroll
-            for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int sl = s0 + 32 * kb2 + 16 * (r >> 3) + 8 * half + (r & 7);
-                    if (sl > lim) sacc[kb2][r] = -INFINITY;
-                }
-        }
-        float mt = -INFINITY;
-#pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb2][r]);
-        mt = half_max(mt);
-        const float m_new = fmaxf(m, mt);
-        if (__ballot((m_new - m) * cl2 > 8.0f) != 0ull) {
-            const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m - m_new) * cl2);
-            l *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-            m = m_new;
-        }
-        const float mc = m == -INFINITY ? 0.0f : m * cl2;   // no visible key yet: every p is 0
-#pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2) {
-            bf16x8 vf[DB][2];
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int k16 = 0; k16 < 2; ++k16)
-                    vf[db][k16] = vfrag(buf, db, 32 * kb2 + 16 * k16);
-            bf16x8 pf[2];
-#pragma unroll
-            for (int k16 = 0; k16 < 2; ++k16) {
-                u32x4 w;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e], cl2, -mc));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e + 1], cl2, -mc));
-                    l += p0 + p1;
-                    w[e] = pack_bf16x2(p0, p1);
-                }
-                pf[k16] = __builtin_bit_cast(bf16x8, w);
-            }
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int k16 = 0; k16 < 2; ++k16)
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][k16], pf[k16], o[db], 0, 0, 0);
-        }
-        // scheduling of the branch-free region: V reads, block 0's exponentials,
-        // then block 0's P.V MFMAs interleaved with block 1's exponentials
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 40, 0);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    };
-
     // Every prefetch is unconditional, with its tile index clamped to the last
     // tile this workgroup reads (always in bounds; the extra copy is never
     // stashed): the same loads are then in flight on every path, so the
@@ -477,13 +390,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
         };
         const int s0 = t * KT;
         if (wave_active && s0 <= n_s + w_tmax) {
-            if (KVSEL_ATTN_PIPE) {
-                if (s0 + KT > n_s + w_tmin + 1) tile_pipe(buf, s0, std::true_type{}, mid);
-                else tile_pipe(buf, s0, std::false_type{}, mid);
-            } else {
-                if (s0 + KT > n_s + w_tmin + 1) tile(buf, s0, std::true_type{}, mid);
-                else tile(buf, s0, std::false_type{}, mid);
-            }
+            if (s0 + KT > n_s + w_tmin + 1) tile(buf, s0, std::true_type{}, mid);
+            else tile(buf, s0, std::false_type{}, mid);
         } else {
             mid();
         }
@@ -973,14 +881,10 @@ hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const
                        const AttnGather* gather) {
     const int bgs = s.batch * s.h_kv;
     if (s.esz == 2) {
-        // 8-wave workgroups share one staged copy of every K/V tile; fall back to
-        // 4 waves when that would leave fewer than 256 workgroups
-        const int rb8 = (s.G * s.C + 255) / 256, rb4 = (s.G * s.C + 127) / 128;
-        const bool pp = !gather && attn_use_pp(s);
-        const bool w8 = !gather && !pp && KVSEL_ATTN_WAVES == 8 && bgs * rb8 >= 256;
-        const int row_blocks = (w8 || pp) ? rb8 : rb4;
-        const int ksplit = w8 ? 1 : attn_ksplit(s);
-        dim3 grid(bgs * row_blocks * ksplit), block((w8 || pp) ? 512 : 256);
+        const bool pp = !gather && attn_use_pp(s);             // 8 waves x 32 rows, else 4 waves
+        const int row_blocks = (s.G * s.C + (pp ? 255 : 127)) / (pp ? 256 : 128);
+        const int ksplit = attn_ksplit(s);
+        dim3 grid(bgs * row_blocks * ksplit), block(pp ? 512 : 256);
         const float cl2 = scale * 1.4426950408889634f;
         const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)kall, *vv = (const uint16_t*)vall;
         const AttnGather ga = gather ? *gather : AttnGather{};
@@ -993,11 +897,9 @@ hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const
         } else if (pp) {
             if (out_f32) KVSEL_ATTN_PPK(128, true); else KVSEL_ATTN_PPK(128, false);
         } else if (s.d == 128) {
-            if (w8) { if (out_f32) KVSEL_ATTN(128, true, 8); else KVSEL_ATTN(128, false, 8); }
-            else { if (out_f32) KVSEL_ATTN(128, true, 4); else KVSEL_ATTN(128, false, 4); }
+            if (out_f32) KVSEL_ATTN(128, true, 4); else KVSEL_ATTN(128, false, 4);
         } else {
-            if (w8) { if (out_f32) KVSEL_ATTN(64, true, 8); else KVSEL_ATTN(64, false, 8); }
-            else { if (out_f32) KVSEL_ATTN(64, true, 4); else KVSEL_ATTN(64, false, 4); }
+            if (out_f32) KVSEL_ATTN(64, true, 4); else KVSEL_ATTN(64, false, 4);
         }
 #undef KVSEL_ATTN
 #undef KVSEL_ATTN_G
