@@ -314,6 +314,8 @@ def test_bitwise_deterministic():
 @pytest.mark.parametrize("C,Ts,B", [
     (200, [0, 400, 1600], 600),        # packed attention (G*C = 800): no prior, T <= B, selection
     (30, [0, 60, 300], 90),            # gathering attention (G*C = 120)
+    (200, [600, 800], 600),            # T = B exactly (everything kept), T = B + one chunk
+    (30, [90, 120, 150], 90),          # the same edge with the gathering attention
 ])
 def test_batched_prefill_ragged(C, Ts, B):
     """Several sequences in one kvsel_prefill_chunk call, each with its own
