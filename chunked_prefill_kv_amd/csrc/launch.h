@@ -68,6 +68,9 @@ hipError_t launch_topk(int problems, int heads_per_seq, const float* scores, int
 // `part` itself).  scratch: topb_scratch_bytes(); its histogram part
 // (problems * 4096 uint32 at its start) must be zero on entry when
 // any_select (launch_qstats clears it).
+// Compute units of the current device (queried once per device; 256 if the
+// query fails).  Launch shapes that run in rounds are sized with it.
+int device_cus();
 int topb_segments(int64_t t_max, int64_t budget);
 size_t topb_scratch_bytes(int problems, int64_t t_max, int64_t budget);
 hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int nsplit, int64_t split_stride,

@@ -322,17 +322,33 @@ hipError_t launch_scan(const SelShape& s, const void* qsel, const float* rq, con
         if (s.d == 128) hipLaunchKernelGGL((scan_rows16_kernel<128, GR>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride);
         else hipLaunchKernelGGL((scan_rows16_kernel<64, GR>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride);
     } else if (s.esz == 2) {
-        // 32-key blocks per wave: kScanNB for bf16 query rows; 2 for [hi | lo]
-        // pairs (twice the query fragments per key block)
-        const int nb = s.qsplit ? 2 : kScanNB;
+        // 32-key blocks per wave: 2 for [hi | lo] query pairs (twice the query
+        // fragments per key block); for bf16 rows 3 or 2, whichever gives the
+        // shorter launch: the workgroups of a launch run in rounds of two per
+        // CU, and a last round that is mostly empty costs a whole round, so
+        // the estimate is rounds x keys per wave, with 3 blocks counted 15%
+        // faster per key than 2 (this weight matches the measured choice on
+        // the three prefill layers: 3 blocks always won on the 128K layer,
+        // whose launches span many rounds)
+        int nb = 2;
+        if (!s.qsplit) {
+            const int64_t slots = 2 * int64_t(device_cus());
+            auto est = [&](int b) {
+                const int64_t wgs = int64_t(bgs) * ((s.t_max + 128 * b - 1) / (128 * b)) * s.nsplit;
+                return double((wgs + slots - 1) / slots) * b * (b == 3 ? 0.85 : 1.0);
+            };
+            nb = kScanNB == 3 && est(3) <= est(2) ? 3 : 2;
+        }
         const int tiles = static_cast<int>((s.t_max + 4 * nb * 32 - 1) / (4 * nb * 32));
         dim3 grid(bgs * tiles * s.nsplit), block(256);
         const int64_t split_stride = int64_t(bgs) * s_stride;
 #define KVSEL_SCAN(D, NB, QK) hipLaunchKernelGGL((scan_mfma_kernel<D, NB, QK>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, s.nsplit, S, s_stride, split_stride)
         if (s.qsplit) {
             if (s.d == 128) KVSEL_SCAN(128, 2, 2); else KVSEL_SCAN(64, 2, 2);
+        } else if (nb == 3) {
+            if (s.d == 128) KVSEL_SCAN(128, 3, 1); else KVSEL_SCAN(64, 3, 1);
         } else {
-            if (s.d == 128) KVSEL_SCAN(128, kScanNB, 1); else KVSEL_SCAN(64, kScanNB, 1);
+            if (s.d == 128) KVSEL_SCAN(128, 2, 1); else KVSEL_SCAN(64, 2, 1);
         }
 #undef KVSEL_SCAN
     } else {
