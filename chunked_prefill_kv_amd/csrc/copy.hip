@@ -100,8 +100,11 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(PackArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) void pack_bf16_kernel(PackArgs a) {
     constexpr int PPR = D / 8;            // 16-byte pieces per row
-    constexpr int LDV = D + 8;            // padded LDS row (bf16)
-    __shared__ __attribute__((aligned(16))) uint16_t vt[kTile * LDV];
+    // LDS tile of V rows [slot][D]; piece c of row r sits at piece c ^ ((r / 8) % PPR),
+    // so the transposed reads below (8 rows 8 apart, one piece column) hit 8
+    // different pieces and the row writes stay a permutation of the row
+    __shared__ __attribute__((aligned(16))) uint16_t vt[kTile * D];
+    static_assert(PPR >= 8, "the swizzle needs 8 distinct pieces per row");
     const int bg = blockIdx.x / a.tiles, tile = blockIdx.x % a.tiles;
     const int b = bg / a.h_kv, g = bg % a.h_kv;
     int64_t T;
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(PackArgs a) {
         const int r = p / PPR, c = p % PPR;
         const int s = tile * kTile + r;
         reinterpret_cast<u32x4*>(a.kall + (static_cast<int64_t>(bg) * a.nk_pad + s) * (D * 2))[c] = kv[i];
-        *reinterpret_cast<u32x4*>(&vt[r * LDV + c * 8]) = vv[i];
+        *reinterpret_cast<u32x4*>(&vt[r * D + ((c ^ ((r >> 3) & (PPR - 1))) * 8)]) = vv[i];
         if (a.append && s >= nsel_b && s < nsel_b + a.C) {
             const int64_t off = a.cv.row_offset(b, g, T + (s - nsel_b));
             reinterpret_cast<u32x4*>(a.cv.k + off)[c] = kv[i];
@@ -137,11 +140,12 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(PackArgs a) {
     uint16_t* vout = reinterpret_cast<uint16_t*>(a.vall) + static_cast<int64_t>(bg) * D * a.nk_pad + tile * kTile;
     for (int p = threadIdx.x; p < D * (kTile / 8); p += 256) {
         const int d = p / (kTile / 8), j = p % (kTile / 8);
+        const int col = (((d >> 3) ^ j) << 3) + (d & 7);     // rows 8j .. 8j+7 share the swizzle j
         u32x4 w;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = vt[(8 * j + 2 * i) * LDV + d];
-            const uint32_t hi = vt[(8 * j + 2 * i + 1) * LDV + d];
+            const uint32_t lo = vt[(8 * j + 2 * i) * D + col];
+            const uint32_t hi = vt[(8 * j + 2 * i + 1) * D + col];
             w[i] = lo | (hi << 16);
         }
         *reinterpret_cast<u32x4*>(vout + static_cast<int64_t>(d) * a.nk_pad + 8 * j) = w;
