@@ -79,10 +79,14 @@ hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int n
                        const CacheView* cv = nullptr, int32_t* rowidx = nullptr);
 
 // Gather the kept query rows of every head into Q_sel[b][g][hh*nq_pad + r][d]
-// (raw rows) and rq = 1/|q|; rows r >= nqp repeat row 0 of that head.
-hipError_t launch_pack_qsel(const SelShape& s, const void* q, const int32_t* keep, int64_t keep_stride,
+// (raw rows) and rq = 1/|q|; rows r >= nqp repeat row 0 of that head.  With
+// keep_all (every chunk query kept, nqp == C: step 1 has nothing to choose and
+// launch_qstats / launch_topk are not run) the kept list is the identity,
+// written to keep when keep is not NULL, 1/|q| is computed here, and
+// zero[0..zero_n) is cleared in place of launch_qstats.
+hipError_t launch_pack_qsel(const SelShape& s, const void* q, int32_t* keep, int64_t keep_stride,
                             const float* qrn, const int64_t* prior_len, void* qsel, float* rq,
-                            hipStream_t st);
+                            hipStream_t st, bool keep_all = false, uint32_t* zero = nullptr, int64_t zero_n = 0);
 
 // Group-pooled step 1 (s.pool == 1): qbar[b][g][i][d] fp32 = mean over the G
 // query heads of g of the unit query rows (sequences with T_b <= budget

@@ -347,20 +347,25 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pack_qsel_kernel(const T* __restrict__ q, int h_q, int G, int C, int nqp,
-                                                        int nq_pad, int rblocks, const int32_t* __restrict__ keep,
+                                                        int nq_pad, int rblocks, int32_t* __restrict__ keep,
                                                         int64_t keep_stride, const float* __restrict__ qrn,
                                                         const int64_t* __restrict__ prior_len, int64_t budget,
-                                                        T* __restrict__ qsel, float* __restrict__ rq) {
+                                                        T* __restrict__ qsel, float* __restrict__ rq, int keep_all,
+                                                        uint32_t* __restrict__ zero, int64_t zero_n) {
     constexpr int kPieces = D * sizeof(T) / 16;          // 16-byte pieces per row
     constexpr int kRows = 32;                            // rows per workgroup
     constexpr int PPT = kRows * kPieces / 256;           // pieces per thread
+    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < zero_n; i += int64_t(gridDim.x) * 256) zero[i] = 0;
     const int bh = blockIdx.x / rblocks, rb = blockIdx.x % rblocks;
     const int b = bh / h_q, h = bh % h_q;
     if (prior_len[b] <= budget) return;
     const int g = h / G, hh = h % G;
     const int h_kv = h_q / G;
     const int64_t dst_row0 = (static_cast<int64_t>(b) * h_kv + g) * G * nq_pad + static_cast<int64_t>(hh) * nq_pad;
-    const int32_t* kp = keep + static_cast<int64_t>(bh) * keep_stride;
+    int32_t* kp = keep + static_cast<int64_t>(bh) * keep_stride;
+    // kept token of row r (rows past nqp repeat row 0); with every query kept
+    // (nqp == C) the list is the identity and the statistics were not run
+    auto kept = [&](int r) { return keep_all ? (r < nqp ? r : 0) : kp[r < nqp ? r : 0]; };
     u32x4 v[PPT];
     int rr[PPT];
 #pragma unroll
@@ -368,10 +373,7 @@ __global__ __launch_bounds__(256) void pack_qsel_kernel(const T* __restrict__ q,
         const int p = threadIdx.x + 256 * i;
         const int r = rb * kRows + p / kPieces, pc = p % kPieces;
         rr[i] = r;
-        if (r < nq_pad) {
-            const int t = kp[r < nqp ? r : 0];
-            v[i] = reinterpret_cast<const u32x4*>(q + (static_cast<int64_t>(bh) * C + t) * D)[pc];
-        }
+        if (r < nq_pad) v[i] = reinterpret_cast<const u32x4*>(q + (static_cast<int64_t>(bh) * C + kept(r)) * D)[pc];
     }
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
@@ -379,9 +381,40 @@ __global__ __launch_bounds__(256) void pack_qsel_kernel(const T* __restrict__ q,
         const int r = rr[i], pc = p % kPieces;
         if (r < nq_pad) reinterpret_cast<u32x4*>(qsel + (dst_row0 + r) * D)[pc] = v[i];
     }
-    if (threadIdx.x < kRows) {
+    if (keep_all) {
+        // 1/|q| of each row from its pieces: squares summed in fp64 (exact for
+        // bf16 and fp32 inputs at these sizes), reduced over the row's lanes
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int p = threadIdx.x + 256 * i;
+            const int r = rr[i], pc = p % kPieces;
+            double n2 = 0.0;
+            if (r < nq_pad) {
+                float x[16 / sizeof(T)];
+                if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[2 * e] = __uint_as_float(v[i][e] << 16);
+                        x[2 * e + 1] = __uint_as_float(v[i][e] & 0xFFFF0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(v[i][e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 16 / static_cast<int>(sizeof(T)); ++e) n2 += static_cast<double>(x[e]) * x[e];
+            }
+#pragma unroll
+            for (int o = kPieces / 2; o >= 1; o >>= 1) n2 += __shfl_xor(n2, o, kWave);
+            if (pc == 0 && r < nq_pad) {
+                const double nq = sqrt(n2);
+                rq[dst_row0 + r] = nq > 0.0 ? static_cast<float>(1.0 / nq) : 0.0f;
+                if (keep && r < nqp) kp[r] = r;
+            }
+        }
+    } else if (threadIdx.x < kRows) {
         const int r = rb * kRows + threadIdx.x;
-        if (r < nq_pad) rq[dst_row0 + r] = qrn[static_cast<int64_t>(bh) * C + kp[r < nqp ? r : 0]];
+        if (r < nq_pad) rq[dst_row0 + r] = qrn[static_cast<int64_t>(bh) * C + kept(r)];
     }
 }
 
@@ -422,17 +455,22 @@ hipError_t launch_topk(int problems, int heads_per_seq, const float* scores, int
     return hipGetLastError();
 }
 
-hipError_t launch_pack_qsel(const SelShape& s, const void* q, const int32_t* keep, int64_t keep_stride,
-                            const float* qrn, const int64_t* prior_len, void* qsel, float* rq, hipStream_t st) {
+hipError_t launch_pack_qsel(const SelShape& s, const void* q, int32_t* keep, int64_t keep_stride,
+                            const float* qrn, const int64_t* prior_len, void* qsel, float* rq, hipStream_t st,
+                            bool keep_all, uint32_t* zero, int64_t zero_n) {
     const int rblocks = (s.nq_pad + 31) / 32;
     dim3 grid(s.batch * s.h_q * rblocks), block(256);
+    const int ka = keep_all ? 1 : 0;
+    if (!keep_all) zero_n = 0;
+#define KVSEL_PACKQ(T, D) hipLaunchKernelGGL((pack_qsel_kernel<T, D>), grid, block, 0, st, (const T*)q, s.h_q, s.G, s.C, s.nqp, s.nq_pad, rblocks, keep, keep_stride, qrn, prior_len, s.budget, (T*)qsel, rq, ka, zero, zero_n)
     if (s.esz == 2) {
-        if (s.d == 128) hipLaunchKernelGGL((pack_qsel_kernel<uint16_t, 128>), grid, block, 0, st, (const uint16_t*)q, s.h_q, s.G, s.C, s.nqp, s.nq_pad, rblocks, keep, keep_stride, qrn, prior_len, s.budget, (uint16_t*)qsel, rq);
-        else hipLaunchKernelGGL((pack_qsel_kernel<uint16_t, 64>), grid, block, 0, st, (const uint16_t*)q, s.h_q, s.G, s.C, s.nqp, s.nq_pad, rblocks, keep, keep_stride, qrn, prior_len, s.budget, (uint16_t*)qsel, rq);
+        if (s.d == 128) KVSEL_PACKQ(uint16_t, 128);
+        else KVSEL_PACKQ(uint16_t, 64);
     } else {
-        if (s.d == 128) hipLaunchKernelGGL((pack_qsel_kernel<float, 128>), grid, block, 0, st, (const float*)q, s.h_q, s.G, s.C, s.nqp, s.nq_pad, rblocks, keep, keep_stride, qrn, prior_len, s.budget, (float*)qsel, rq);
-        else hipLaunchKernelGGL((pack_qsel_kernel<float, 64>), grid, block, 0, st, (const float*)q, s.h_q, s.G, s.C, s.nqp, s.nq_pad, rblocks, keep, keep_stride, qrn, prior_len, s.budget, (float*)qsel, rq);
+        if (s.d == 128) KVSEL_PACKQ(float, 128);
+        else KVSEL_PACKQ(float, 64);
     }
+#undef KVSEL_PACKQ
     return hipGetLastError();
 }
 

@@ -25,6 +25,7 @@ SMALL = {
     "bf16_nq1": LLAMA.replace(L=1500, C=300, H_q=8, H_kv=2, n_q=1, B=400),               # one kept query per head
     "bf16_budget1": LLAMA.replace(L=1024, C=256, H_q=4, H_kv=2, n_q=8, B=1),
     "bf16_keep_all_queries": LLAMA.replace(L=1200, C=100, H_q=4, H_kv=1, n_q=128, B=150),
+    "f32_keep_all_queries": TINY.replace(L=512, C=64, n_q=100, B=100),                  # N_q >= C, fp32 rows
     "bf16_dense": LLAMA.replace(L=1000, C=250, H_q=8, H_kv=2, n_q=16, B=1000),           # B >= T always
     "bf16_short_chunks": LLAMA.replace(L=600, C=25, H_q=8, H_kv=2, n_q=10, B=150),      # G*C <= 128: gathering attention
 }
