@@ -114,7 +114,7 @@ __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
     __shared__ int cj[kCap];
     __shared__ uint32_t sgt[1024], seq_[1024];      // per-segment counts (nseg <= 1024)
     __shared__ uint32_t wsum[16];
-    __shared__ uint32_t s_bin, s_need, s_cnt, s_tau, s_needeq, s_digit, s_rem;
+    __shared__ uint32_t s_bin, s_need, s_cnt, s_digit, s_rem;
     const uint32_t* h = a.hist + static_cast<int64_t>(p) * kBins;
     for (int i = tid; i < kBins; i += 1024) hs[i] = h[i];
     for (int i = tid; i < a.nseg; i += 1024) { sgt[i] = 0; seq_[i] = 0; }
@@ -182,7 +182,25 @@ __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
     };
     const int n_scan = in_lds ? static_cast<int>(cnt) : T;
     uint32_t prefix = 0, remaining = need;
-    for (int bits = 32; bits > 0;) {
+    int bits0 = 32;
+    if (in_lds) {
+        // the boundary keys share one value bin, so their leading bits agree:
+        // the radix passes start below the highest bit in which any differs
+        const uint32_t first = ck[0];
+        uint32_t diff = 0;
+        for (int i = tid; i < n_scan; i += 1024) diff |= ck[i] ^ first;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) diff |= __shfl_xor(diff, o, kWave);
+        if (lane == 0) wsum[wave] = diff;
+        __syncthreads();
+        diff = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) diff |= wsum[w];
+        __syncthreads();
+        bits0 = diff ? 32 - __clz(diff) : 0;
+        prefix = bits0 == 32 ? 0u : (first >> bits0) << bits0;
+    }
+    for (int bits = bits0; bits > 0;) {
         const int w = bits < 11 ? bits : 11, shift = bits - w;
         for (int i = tid; i < 2048; i += 1024) hs[i] = 0;
         __syncthreads();
