@@ -88,6 +88,18 @@ __global__ __launch_bounds__(256) void qcos_kernel(const T* __restrict__ q, int 
     constexpr int RPP = 256 / G8;
     const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
     if (prior_len[bh / h_q] <= budget) return;
+    // this block's query rows are loaded first, so they arrive while the mean is formed
+    const int c8 = threadIdx.x % G8, sub = threadIdx.x / G8;
+    const T* qh = q + static_cast<int64_t>(bh) * C * D;
+    const int r1 = min(C, (blk + 1) * kQRows);
+    constexpr int NIT = kQRows / RPP;
+    float x[NIT][8];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int r = blk * kQRows + sub + it * RPP;
+        if (r < r1) Vec8<T>::load(qh + static_cast<int64_t>(r) * D + c8 * 8, x[it]);
+        else for (int i = 0; i < 8; ++i) x[it][i] = 0.0f;
+    }
     __shared__ double mean[D];
     __shared__ double mnorm;
     if (threadIdx.x < D) {
@@ -111,21 +123,10 @@ __global__ __launch_bounds__(256) void qcos_kernel(const T* __restrict__ q, int 
         if (threadIdx.x == 0) mnorm = sqrt(s);
     }
     __syncthreads();
-    const int c8 = threadIdx.x % G8, sub = threadIdx.x / G8;
     double m[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) m[i] = mean[c8 * 8 + i];
     const double mn = mnorm;
-    const T* qh = q + static_cast<int64_t>(bh) * C * D;
-    const int r1 = min(C, (blk + 1) * kQRows);
-    constexpr int NIT = kQRows / RPP;
-    float x[NIT][8];
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {           // all loads in flight first
-        const int r = blk * kQRows + sub + it * RPP;
-        if (r < r1) Vec8<T>::load(qh + static_cast<int64_t>(r) * D + c8 * 8, x[it]);
-        else for (int i = 0; i < 8; ++i) x[it][i] = 0.0f;
-    }
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {           // uniform trip count: shuffles stay converged
         const int r = blk * kQRows + sub + it * RPP;
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(256) void qcos_kernel(const T* __restrict__ q, int 
 // ----------------------------------------------------------------------------- exact top-k
 
 #ifndef KVSEL_TOPK_THREADS
-#define KVSEL_TOPK_THREADS 1024
+#define KVSEL_TOPK_THREADS 512
 #endif
 constexpr int kTopkThreads = KVSEL_TOPK_THREADS;
 constexpr int kTopkWaves = kTopkThreads / kWave;
