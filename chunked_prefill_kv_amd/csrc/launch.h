@@ -43,9 +43,11 @@ inline int scan_splits(int batch, int h_kv, int G, int64_t t_max) {
 // clears zero[0..zero_n) (the top-B histogram) for the kernels that follow.
 hipError_t launch_qstats(const SelShape& s, const void* q, const int64_t* prior_len, double* part,
                          float* qcos, float* qrn, uint32_t* zero, int64_t zero_n, hipStream_t st);
-constexpr int kQRows = 128;   // query rows per statistics workgroup
+// query rows per statistics workgroup: 64 when that still gives fewer than
+// about 1024 workgroups (more loads in flight per CU), else 128
+constexpr int kQRowsMin = 64;
 inline int64_t qstats_part_elems(const SelShape& s) {
-    return int64_t(s.batch) * s.h_q * ((s.C + kQRows - 1) / kQRows) * s.d;
+    return int64_t(s.batch) * s.h_q * ((s.C + kQRowsMin - 1) / kQRowsMin) * s.d;
 }
 
 // Exact top-k with lower-index tie-break, indices ascending, -1 padded to k.

@@ -41,7 +41,7 @@ template <> struct Vec8<float> {      // 8 fp32 = two 16-byte loads
 
 
 // pass 1: per (head, row block) column sums of the query rows -> part[bh][blk][D] (fp64)
-template <typename T, int D>
+template <typename T, int D, int QR>
 __global__ __launch_bounds__(256) void qsum_kernel(const T* __restrict__ q, int h_q, int C, int nblk,
                                                    const int64_t* __restrict__ prior_len, int64_t budget,
                                                    double* __restrict__ part, uint32_t* __restrict__ zero,
@@ -54,12 +54,12 @@ __global__ __launch_bounds__(256) void qsum_kernel(const T* __restrict__ q, int 
     const T* qh = q + static_cast<int64_t>(bh) * C * D;
     const int c8 = threadIdx.x % G8, sub = threadIdx.x / G8;
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const int r1 = min(C, (blk + 1) * kQRows);
-    constexpr int NIT = kQRows / RPP;
+    const int r1 = min(C, (blk + 1) * QR);
+    constexpr int NIT = QR / RPP;
     float x[NIT][8];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {           // all loads in flight first
-        const int r = blk * kQRows + sub + it * RPP;
+        const int r = blk * QR + sub + it * RPP;
         if (r < r1) Vec8<T>::load(qh + static_cast<int64_t>(r) * D + c8 * 8, x[it]);
         else for (int i = 0; i < 8; ++i) x[it][i] = 0.0f;
     }
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void qsum_kernel(const T* __restrict__ q, int 
 }
 
 // pass 2: mean query from the partial sums, then cos(q_i, mean) and 1/|q_i| per row
-template <typename T, int D>
+template <typename T, int D, int QR>
 __global__ __launch_bounds__(256) void qcos_kernel(const T* __restrict__ q, int h_q, int C, int nblk,
                                                    const int64_t* __restrict__ prior_len, int64_t budget,
                                                    const double* __restrict__ part, float* __restrict__ qcos,
@@ -91,12 +91,12 @@ __global__ __launch_bounds__(256) void qcos_kernel(const T* __restrict__ q, int 
     // this block's query rows are loaded first, so they arrive while the mean is formed
     const int c8 = threadIdx.x % G8, sub = threadIdx.x / G8;
     const T* qh = q + static_cast<int64_t>(bh) * C * D;
-    const int r1 = min(C, (blk + 1) * kQRows);
-    constexpr int NIT = kQRows / RPP;
+    const int r1 = min(C, (blk + 1) * QR);
+    constexpr int NIT = QR / RPP;
     float x[NIT][8];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-        const int r = blk * kQRows + sub + it * RPP;
+        const int r = blk * QR + sub + it * RPP;
         if (r < r1) Vec8<T>::load(qh + static_cast<int64_t>(r) * D + c8 * 8, x[it]);
         else for (int i = 0; i < 8; ++i) x[it][i] = 0.0f;
     }
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void qcos_kernel(const T* __restrict__ q, int 
     const double mn = mnorm;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {           // uniform trip count: shuffles stay converged
-        const int r = blk * kQRows + sub + it * RPP;
+        const int r = blk * QR + sub + it * RPP;
         double dot = 0.0, n2 = 0.0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -423,22 +423,29 @@ __global__ __launch_bounds__(256) void pack_qsel_kernel(const T* __restrict__ q,
 
 hipError_t launch_qstats(const SelShape& s, const void* q, const int64_t* prior_len, double* part, float* qcos,
                          float* qrn, uint32_t* zero, int64_t zero_n, hipStream_t st) {
-    const int nblk = (s.C + kQRows - 1) / kQRows;
+    const int qr = int64_t(s.batch) * s.h_q * ((s.C + 127) / 128) < 1024 ? kQRowsMin : 128;
+    const int nblk = (s.C + qr - 1) / qr;
     dim3 grid(s.batch * s.h_q * nblk), block(256);
-#define KVSEL_QSTATS(T, D)                                                                                         \
+#define KVSEL_QSTATS(T, D, QR)                                                                                     \
     do {                                                                                                           \
-        hipLaunchKernelGGL((qsum_kernel<T, D>), grid, block, 0, st, (const T*)q, s.h_q, s.C, nblk, prior_len,      \
+        hipLaunchKernelGGL((qsum_kernel<T, D, QR>), grid, block, 0, st, (const T*)q, s.h_q, s.C, nblk, prior_len,  \
                            s.budget, part, zero, zero_n);                                                          \
-        hipLaunchKernelGGL((qcos_kernel<T, D>), grid, block, 0, st, (const T*)q, s.h_q, s.C, nblk, prior_len,      \
+        hipLaunchKernelGGL((qcos_kernel<T, D, QR>), grid, block, 0, st, (const T*)q, s.h_q, s.C, nblk, prior_len,  \
                            s.budget, part, qcos, qrn);                                                             \
     } while (0)
+#define KVSEL_QSTATS_R(T, D)                                                                                       \
+    do {                                                                                                           \
+        if (qr == kQRowsMin) KVSEL_QSTATS(T, D, kQRowsMin);                                                        \
+        else KVSEL_QSTATS(T, D, 128);                                                                              \
+    } while (0)
     if (s.esz == 2) {
-        if (s.d == 128) KVSEL_QSTATS(uint16_t, 128);
-        else KVSEL_QSTATS(uint16_t, 64);
+        if (s.d == 128) KVSEL_QSTATS_R(uint16_t, 128);
+        else KVSEL_QSTATS_R(uint16_t, 64);
     } else {
-        if (s.d == 128) KVSEL_QSTATS(float, 128);
-        else KVSEL_QSTATS(float, 64);
+        if (s.d == 128) KVSEL_QSTATS_R(float, 128);
+        else KVSEL_QSTATS_R(float, 64);
     }
+#undef KVSEL_QSTATS_R
 #undef KVSEL_QSTATS
     return hipGetLastError();
 }
