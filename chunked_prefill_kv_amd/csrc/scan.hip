@@ -34,8 +34,17 @@ namespace kvsel {
 // workgroups when the cache or the KV head count is small); split s writes
 // the sum over its heads, scaled by 1/G, to S + s * split_stride and the top-B
 // kernel adds the splits in order.
+#ifndef KVSEL_SCAN_NB4
+#define KVSEL_SCAN_NB4 1        // four 32-key blocks per wave where that fills the CUs best
+#endif
+#ifndef KVSEL_SCAN_W4
+#define KVSEL_SCAN_W4 0.78      // its time per key relative to two blocks
+#endif
+#ifndef KVSEL_SCAN_OCC
+#define KVSEL_SCAN_OCC 2        // workgroups per CU the register budget is sized for
+#endif
 template <int D, int NB, int QK>
-__global__ __launch_bounds__(256, 2) void scan_mfma_kernel(const uint16_t* __restrict__ qsel,
+__global__ __launch_bounds__(256, KVSEL_SCAN_OCC) void scan_mfma_kernel(const uint16_t* __restrict__ qsel,
                                                            const float* __restrict__ rq, CacheView cv,
                                                            const int64_t* __restrict__ prior_len, int64_t budget,
                                                            int h_kv, int G, int nq_pad, int tiles, int nsplit,
@@ -335,9 +344,10 @@ hipError_t launch_scan(const SelShape& s, const void* qsel, const float* rq, con
             const int64_t slots = 2 * int64_t(device_cus());
             auto est = [&](int b) {
                 const int64_t wgs = int64_t(bgs) * ((s.t_max + 128 * b - 1) / (128 * b)) * s.nsplit;
-                return double((wgs + slots - 1) / slots) * b * (b == 3 ? 0.85 : 1.0);
+                return double((wgs + slots - 1) / slots) * b * (b == 4 ? KVSEL_SCAN_W4 : b == 3 ? 0.85 : 1.0);
             };
             nb = kScanNB == 3 && est(3) <= est(2) ? 3 : 2;
+            if (KVSEL_SCAN_NB4 && est(4) < est(nb)) nb = 4;
         }
         const int tiles = static_cast<int>((s.t_max + 4 * nb * 32 - 1) / (4 * nb * 32));
         dim3 grid(bgs * tiles * s.nsplit), block(256);
@@ -345,6 +355,8 @@ hipError_t launch_scan(const SelShape& s, const void* qsel, const float* rq, con
 #define KVSEL_SCAN(D, NB, QK) hipLaunchKernelGGL((scan_mfma_kernel<D, NB, QK>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, s.nsplit, S, s_stride, split_stride)
         if (s.qsplit) {
             if (s.d == 128) KVSEL_SCAN(128, 2, 2); else KVSEL_SCAN(64, 2, 2);
+        } else if (nb == 4) {
+            if (s.d == 128) KVSEL_SCAN(128, 4, 1); else KVSEL_SCAN(64, 4, 1);
         } else if (nb == 3) {
             if (s.d == 128) KVSEL_SCAN(128, 3, 1); else KVSEL_SCAN(64, 3, 1);
         } else {
