@@ -74,31 +74,6 @@ __global__ __launch_bounds__(256, KVSEL_SCAN_OCC) void scan_mfma_kernel(const ui
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const int half = lane >> 5, col = lane & 31;
 
-    // ---- this wave's keys: fragments + reciprocal norms
-    bf16x8 kf[NB][KS];
-    float rk[NB];
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
-        const int64_t key = key0 + (wave * NB + kb) * 32 + col;
-        const bool valid = key < T;
-        const char* row = cv.k + (valid ? cv.row_offset(b, g, key) : 0);
-        float n2 = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 raw = {0u, 0u, 0u, 0u};
-            if (valid) raw = *reinterpret_cast<const u32x4*>(row + (16 * ks + 8 * half) * 2);
-            kf[kb][ks] = __builtin_bit_cast(bf16x8, raw);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float lo = __uint_as_float(raw[i] << 16), hi = __uint_as_float(raw[i] & 0xFFFF0000u);
-                n2 = fmaf(lo, lo, n2);
-                n2 = fmaf(hi, hi, n2);
-            }
-        }
-        n2 += __shfl_xor(n2, 32, kWave);
-        rk[kb] = n2 > 0.0f ? 1.0f / sqrtf(n2) : 0.0f;
-    }
-
     const int R = G / nsplit * nq_pad;                  // this split's query rows
     const int nstage = (R + STAGE - 1) / STAGE;
     const uint16_t* qb = qsel + (static_cast<int64_t>(bg) * G * nq_pad + static_cast<int64_t>(split) * R) * KQ;
@@ -111,14 +86,12 @@ __global__ __launch_bounds__(256, KVSEL_SCAN_OCC) void scan_mfma_kernel(const ui
         for (int i = 0; i < PPT; ++i) {
             const int p = tid + 256 * i;
             const int r = p / (KQ / 8), c8 = p % (KQ / 8);
-            const int row = s * STAGE + r;
-            pre[i] = row < R ? *reinterpret_cast<const u32x4*>(qb + static_cast<int64_t>(row) * KQ + c8 * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
+            // rows past R (R is a multiple of 32) are never multiplied: their
+            // loads read row R-1, so every load is unconditional
+            const int row = min(s * STAGE + r, R - 1);
+            pre[i] = *reinterpret_cast<const u32x4*>(qb + static_cast<int64_t>(row) * KQ + c8 * 8);
         }
-        if (tid < STAGE) {
-            const int row = s * STAGE + tid;
-            prq = row < R ? rqb[row] : 0.0f;
-        }
+        if (tid < STAGE) prq = rqb[min(s * STAGE + tid, R - 1)];
     };
     auto stash = [&](int buf) {
 #pragma unroll
@@ -134,7 +107,40 @@ __global__ __launch_bounds__(256, KVSEL_SCAN_OCC) void scan_mfma_kernel(const ui
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) { run[kb] = -INFINITY; sum[kb] = 0.0f; }
 
+    // the first query stage is requested before the keys: staging it waits
+    // for those loads only, and the first MFMAs for the first key block only
     fetch(0);
+    // ---- this wave's keys: fragments (their reciprocal norms are taken after
+    // the stage loop, so the first stages do not wait for every key row)
+    // Keys past T read key T-1 (their scores are never written), so every
+    // load is unconditional and the compiler's waits count them exactly.
+    // (Row offsets first: in a paged cache each one waits for a block-table
+    // entry, and no key load then waits behind another block's.)
+    bf16x8 kf[NB][KS];
+    int64_t koff[NB];
+    if (cv.block_size == 0) {
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) koff[kb] = cv.row_offset(b, g, min(key0 + (wave * NB + kb) * 32 + col, T - 1));
+    } else {
+        const uint32_t bs = static_cast<uint32_t>(cv.block_size);
+        int32_t blk[NB];
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) {
+            const uint32_t p = static_cast<uint32_t>(min(key0 + (wave * NB + kb) * 32 + col, T - 1));
+            blk[kb] = cv.block_table[static_cast<int64_t>(b) * cv.max_blocks + p / bs];
+        }
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) {
+            const uint32_t p = static_cast<uint32_t>(min(key0 + (wave * NB + kb) * 32 + col, T - 1));
+            koff[kb] = ((static_cast<int64_t>(blk[kb]) * cv.h_kv + g) * cv.block_size + p % bs) * static_cast<int64_t>(cv.row_bytes);
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            kf[kb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cv.k + koff[kb] + (16 * ks + 8 * half) * 2));
+
     stash(0);
     __syncthreads();
     for (int s = 0; s < nstage; ++s) {
@@ -179,6 +185,23 @@ __global__ __launch_bounds__(256, KVSEL_SCAN_OCC) void scan_mfma_kernel(const ui
         __syncthreads();
     }
 
+    float rk[NB];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+        float n2 = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 raw = __builtin_bit_cast(u32x4, kf[kb][ks]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo = __uint_as_float(raw[i] << 16), hi = __uint_as_float(raw[i] & 0xFFFF0000u);
+                n2 = fmaf(lo, lo, n2);
+                n2 = fmaf(hi, hi, n2);
+            }
+        }
+        n2 += __shfl_xor(n2, 32, kWave);
+        rk[kb] = n2 > 0.0f ? 1.0f / sqrtf(n2) : 0.0f;
+    }
     const float inv_g = 1.0f / static_cast<float>(G);
     float* Sb = S + static_cast<int64_t>(split) * split_stride + static_cast<int64_t>(bg) * s_stride;
 #pragma unroll

@@ -120,14 +120,16 @@ def batch(prior_len_host: Sequence[int], chunk_len: int, prior_len_dev: Optional
     n = len(prior_len_host)
     arr = (ctypes.c_int64 * n)(*[int(x) for x in prior_len_host])
     b = Batch(n, chunk_len, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)), _ptr(prior_len_dev))
-    b._keep = arr            # keep the host array alive with the struct
+    b._keep = (arr, prior_len_dev)   # the struct holds raw pointers: keep both arrays alive with it
     return b
 
 
 def cache(k: torch.Tensor, v: torch.Tensor, capacity: int, block_size: int = 0,
           block_table: Optional[torch.Tensor] = None) -> Cache:
     mb = 0 if block_table is None else block_table.shape[1]
-    return Cache(k.data_ptr(), v.data_ptr(), capacity, block_size, mb, _ptr(block_table))
+    c = Cache(k.data_ptr(), v.data_ptr(), capacity, block_size, mb, _ptr(block_table))
+    c._keep = (k, v, block_table)    # raw pointers in the struct: keep the tensors alive with it
+    return c
 
 
 def workspace_size(h: Heads, b: Batch, p: Params) -> int:

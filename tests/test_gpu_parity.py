@@ -378,3 +378,88 @@ def test_batched_prefill_ragged(C, Ts, B):
         O_or = quoka.attend(Qc, [Kp[g, idx_h[g, :n]] for g in range(wl.H_kv)],
                             [Vp[g, idx_h[g, :n]] for g in range(wl.H_kv)], Kn, Vn)
         parity.check_close(O[s], O_or, parity.o_tol(wl.dtype), f"O seq {s}")
+
+
+@pytest.mark.parametrize("C,Ts,B,bs", [
+    (200, [0, 400, 1600], 600, 16),    # packed attention over a paged cache
+    (30, [60, 300, 990], 90, 16),      # gathering attention: rows through the block table
+    (64, [704, 1536], 300, 24),        # blocks of 24 rows: block boundaries inside key groups
+])
+def test_batched_prefill_paged(C, Ts, B, bs):
+    """Chunks of several tokens over a paged cache (shuffled block table): the
+    same checks as the contiguous batch, and the chunk's rows written to their
+    paged slots."""
+    wl = LLAMA.replace(L=max(Ts) + C, C=C, H_q=8, H_kv=2, n_q=24, B=B)
+    print(f"[case] paged prefill C={C} T={Ts} block={bs}", flush=True)
+    nb = len(Ts)
+    cur = [gen.chunk_inputs(wl, T // C, seq=s) for s, T in enumerate(Ts)]
+    prior = [[gen.chunk_inputs(wl, k, seq=s) for k in range(T // C)] for s, T in enumerate(Ts)]
+    nblk = [(T + C + bs - 1) // bs for T in Ts]
+    perm = np.random.default_rng([0x5EED, 77, C, bs]).permutation(sum(nblk)).astype(np.int32)
+    table = np.zeros((nb, max(nblk)), dtype=np.int32)
+    pos = 0
+    for s in range(nb):
+        table[s, :nblk[s]] = perm[pos:pos + nblk[s]]
+        pos += nblk[s]
+    kpool = np.zeros((sum(nblk), wl.H_kv, bs, wl.d), dtype=np.uint16)
+    vpool = np.zeros_like(kpool)
+    logical = []
+    for s, T in enumerate(Ts):
+        kl = np.zeros((wl.H_kv, nblk[s] * bs, wl.d), dtype=np.uint16)
+        vl = np.zeros_like(kl)
+        if T:
+            kl[:, :T] = np.concatenate([c[1] for c in prior[s]], axis=1)
+            vl[:, :T] = np.concatenate([c[2] for c in prior[s]], axis=1)
+        logical.append((kl[:, :T].copy(), vl[:, :T].copy()))
+        for j in range(nblk[s]):
+            kpool[table[s, j]] = kl[:, j * bs:(j + 1) * bs]
+            vpool[table[s, j]] = vl[:, j * bs:(j + 1) * bs]
+    dev = "cuda"
+    kp_d, vp_d = runner.to_device(kpool, dev), runner.to_device(vpool, dev)
+    table_d = torch.tensor(table, dtype=torch.int32, device=dev)
+    q = runner.to_device(np.stack([c[0] for c in cur]), dev)
+    kn = runner.to_device(np.stack([c[1] for c in cur]), dev)
+    vn = runner.to_device(np.stack([c[2] for c in cur]), dev)
+    h = K.heads(wl.H_q, wl.H_kv, wl.d, K.KVSEL_BF16)
+    p = K.Params(wl.n_q, wl.B)
+    prior_d = torch.tensor(Ts, dtype=torch.int64, device=dev)      # kept alive: the batch holds its pointer
+    b = K.batch(Ts, C, prior_d)
+    cache = K.cache(kp_d, vp_d, kpool.shape[0], bs, table_d)
+    ws = torch.empty(K.workspace_size(h, b, p), dtype=torch.uint8, device=dev)
+    nqp = min(wl.n_q, C)
+    idx = torch.full((nb, wl.H_kv, B), -7, dtype=torch.int32, device=dev)
+    keep = torch.full((nb, wl.H_q, nqp), -7, dtype=torch.int32, device=dev)
+    S = torch.full((nb, wl.H_kv, max(max(Ts), 1)), float("nan"), dtype=torch.float32, device=dev)
+    K.kvsel_select(h, b, p, q, cache, idx, None, None, keep, S, ws)
+    out = torch.empty(nb, wl.H_q, C, wl.d, dtype=torch.float32, device=dev)
+    idx2 = torch.full_like(idx, -7)
+    K.kvsel_prefill_chunk(h, b, p, q, kn, vn, cache, out, idx2, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), idx2.cpu().numpy())
+    kpa, vpa = runner.to_host_bits(kp_d), runner.to_host_bits(vp_d)
+    O = out.double().cpu().numpy()
+    for s, T in enumerate(Ts):
+        # the chunk's rows in their paged slots, the prior rows untouched
+        for t in range(T + C):
+            blk, off = table[s, t // bs], t % bs
+            want_k = cur[s][1][:, t - T] if t >= T else logical[s][0][:, t]
+            want_v = cur[s][2][:, t - T] if t >= T else logical[s][1][:, t]
+            assert np.array_equal(kpa[blk, :, off], want_k) and np.array_equal(vpa[blk, :, off], want_v), (s, t)
+        Qc, Kn, Vn = (gen.to_f64(x) for x in cur[s])
+        Kp, Vp = gen.to_f64(logical[s][0]), gen.to_f64(logical[s][1])
+        idx_h = idx[s].cpu().numpy()
+        if T > B:
+            keep_h = keep[s].cpu().numpy()
+            for hh in range(wl.H_q):
+                parity.check_keep(Qc[hh], wl.n_q, keep_h[hh])
+            S_or = quoka.key_scores(Qc, [np.sort(keep_h[hh]) for hh in range(wl.H_q)], Kp)
+            for g in range(wl.H_kv):
+                parity.check_close(S[s, g, :T].cpu().numpy(), S_or[g], parity.S_TOL, f"S seq {s} head {g}")
+                parity.check_idx(S_or[g], B, idx_h[g], S[s, g, :T].cpu().numpy())
+        else:
+            for g in range(wl.H_kv):
+                assert np.array_equal(idx_h[g, :T], np.arange(T)) and np.all(idx_h[g, T:] == -1)
+        n = min(B, T)
+        O_or = quoka.attend(Qc, [Kp[g, idx_h[g, :n]] for g in range(wl.H_kv)],
+                            [Vp[g, idx_h[g, :n]] for g in range(wl.H_kv)], Kn, Vn)
+        parity.check_close(O[s], O_or, parity.o_tol(wl.dtype), f"O seq {s}")
