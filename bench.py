@@ -32,6 +32,20 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill tokens/s/layer (select+attend) at 32K ctx; % of HBM/MFMA roofline"
 MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
+FP32_VECTOR_PEAK_TFLOPS = 157.3     # MI355X fp32 vector (the fp32 path's attention runs on the VALU)
+
+
+def attn_kernel_name(wl) -> str:
+    """The attention kernel the library launches for this shape (the same rule as
+    its launcher: the 8-wave ping-pong kernel for bf16, d = 128, more than one
+    128-row block per KV head, unless the grid of 256-row blocks holds between
+    one and two workgroups per CU)."""
+    if wl.dtype != "bf16":
+        return f"attn_valu_kernel<{wl.d}> (fp32 VALU)"
+    wgs = wl.H_kv * -(-wl.G * wl.C // 256)
+    if wl.d == 128 and wl.G * wl.C > 128 and (wgs < 256 or wgs >= 512):
+        return "attn_pp_kernel<128, bf16 out> (8 waves, ping-pong)"
+    return f"attn_mfma_kernel<{wl.d}, bf16 out, 64, 4> (4 waves)"
 
 
 def measured_traffic(kernel_src: str, summary: str):
@@ -168,13 +182,15 @@ def main():
     att_flop, att_bytes, scan_flop, scan_bytes = algorithmic_work(wl, r.starts, r.lens, args.pooling)
     n_att, ms_att = tr["attn"]
     att_tflops = sum(att_flop) * args.steps / (ms_att * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "achieved": round(att_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(att_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+    bf16 = wl.dtype == "bf16"
+    peak = MFMA_BF16_PEAK_TFLOPS if bf16 else FP32_VECTOR_PEAK_TFLOPS
+    roofline = {"bound": "mfma" if bf16 else "alu", "achieved": round(att_tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(att_tflops / peak, 4),
                 "traffic": measured_traffic(os.path.join(ROOT, "chunked_prefill_kv_amd", "csrc", "attn.hip"),
                                             os.path.join(ROOT, "profiles", "attn_mfma_llama8b_32k_traffic.md"))
                 if wl.name == "llama8b_32k" else None,
                 "algorithmic_bytes_per_launch": sum(att_bytes) / len(att_bytes),
-                "kernel": "attn_mfma_kernel<128,bf16 out>",
+                "kernel": attn_kernel_name(wl),
                 "launches": n_att, "avg_launch_us": round(ms_att * 1e3 / n_att, 2),
                 "algorithmic_flop_per_launch": sum(att_flop) / len(att_flop)}
     kernels = {k: {"ms_per_step": round(v[1] / args.steps, 4), "launches_per_step": v[0] // args.steps}
