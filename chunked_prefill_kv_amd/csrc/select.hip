@@ -102,17 +102,33 @@ __global__ __launch_bounds__(256) void qcos_kernel(const T* __restrict__ q, int 
     }
     __shared__ double mean[D];
     __shared__ double mnorm;
-    if (threadIdx.x < D) {
+    {
+        // column sums of the partials: every thread takes one column and every
+        // NS-th block, 16 loads in flight.  fp64 sums of bf16 rows are exact,
+        // so the order of the additions does not change the mean; for fp32
+        // rows it can only move the last bits of the fp64 mean.
+        constexpr int NS = 256 / D;
+        __shared__ double red[NS][D];
+        const int c = threadIdx.x % D, j = threadIdx.x / D;
         double s = 0.0;
-        for (int k0 = 0; k0 < nblk; k0 += 8) {          // 8 loads in flight, summed in block order
-            double v[8];
+        for (int k0 = j; k0 < nblk; k0 += 16 * NS) {
+            double v[16];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                v[i] = k0 + i < nblk ? part[(static_cast<int64_t>(bh) * nblk + k0 + i) * D + threadIdx.x] : 0.0;
+            for (int i = 0; i < 16; ++i) {
+                const int k = k0 + i * NS;
+                v[i] = k < nblk ? part[(static_cast<int64_t>(bh) * nblk + k) * D + c] : 0.0;
+            }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) s += v[i];
+            for (int i = 0; i < 16; ++i) s += v[i];
         }
-        mean[threadIdx.x] = s / C;
+        red[j][c] = s;
+        __syncthreads();
+        if (threadIdx.x < D) {
+            double m = 0.0;
+#pragma unroll
+            for (int i = 0; i < NS; ++i) m += red[i][threadIdx.x];
+            mean[threadIdx.x] = m / C;
+        }
     }
     __syncthreads();
     if (threadIdx.x < kWave) {
