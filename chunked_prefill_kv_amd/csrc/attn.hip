@@ -59,6 +59,9 @@ __device__ __forceinline__ int sigma(int m) {
 #ifndef KVSEL_ATTN_PP
 #define KVSEL_ATTN_PP 1                   // packed path: ping-pong kernel (8 waves, 256 rows)
 #endif
+#ifndef KVSEL_ATTN_CU_PAIR
+#define KVSEL_ATTN_CU_PAIR 1              // one-round 4-wave grids: long and short row blocks share a CU
+#endif
 
 //
 // GATHER: the key list is read from its sources (kept cache rows through idx,
@@ -71,7 +74,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
                                                            const int32_t* __restrict__ nsel, int nk_pad, int C, int G,
                                                            int h_kv, int row_blocks, float cl2,
                                                            void* __restrict__ out, int ksplit,
-                                                           float* __restrict__ part, AttnGather ga) {
+                                                           float* __restrict__ part, AttnGather ga, int cu_pair) {
     constexpr bool VR = GATHER;             // V tile staged row-major
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
@@ -93,10 +96,22 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
 
     // slot -> (KV head, row block, key split); later row blocks (more keys) first
     const int slot = xcd_slot(blockIdx.x, gridDim.x);
-    const int bg = slot / (row_blocks * ksplit);
+    int bg = slot / (row_blocks * ksplit);
     const int rem = slot % (row_blocks * ksplit);
-    const int rblk = row_blocks - 1 - rem / ksplit;
+    int rblk = row_blocks - 1 - rem / ksplit;
     const int ksp = rem % ksplit;
+    if (cu_pair) {
+        // One round, two workgroups per CU: an XCD's m workgroups are placed
+        // on its CUs in dispatch order, so workgroups p and p + m/2 of the XCD
+        // share a CU, and a CU lasts about as long as the tiles of both.  The
+        // p-th heaviest row block is paired with the p-th lightest (KV heads
+        // of the XCD: m / row_blocks; ksplit is 1 here).
+        const int m = gridDim.x / kXcds, k = m / row_blocks;
+        const int x = slot / m, pp = slot % m;
+        const int q = pp < m / 2 ? pp : m - 1 - (pp - m / 2);
+        rblk = row_blocks - 1 - q / k;
+        bg = x * k + q % k;
+    }
     const int b = bg / h_kv, g = bg % h_kv;
     const int nrows = G * C;
     const int64_t T_b = GATHER ? ga.prior_len[b] : 0;
@@ -885,11 +900,17 @@ hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const
         const int row_blocks = (s.G * s.C + (pp ? 255 : 127)) / (pp ? 256 : 128);
         const int ksplit = attn_ksplit(s);
         dim3 grid(bgs * row_blocks * ksplit), block(pp ? 512 : 256);
+        // 4-wave packed kernel in one round of two workgroups per CU, whole KV
+        // heads per XCD: pair long with short row blocks on each CU
+        const int64_t per_xcd = grid.x / kXcds;
+        const int cu_pair = (KVSEL_ATTN_CU_PAIR && !gather && !pp && ksplit == 1 && row_blocks > 1 &&
+                             grid.x % kXcds == 0 && per_xcd % row_blocks == 0 &&
+                             int64_t(grid.x) <= 2 * int64_t(device_cus())) ? 1 : 0;
         const float cl2 = scale * 1.4426950408889634f;
         const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)kall, *vv = (const uint16_t*)vall;
         const AttnGather ga = gather ? *gather : AttnGather{};
-#define KVSEL_ATTN(D, F32, W) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, KVSEL_ATTN_KT, W, false>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part, ga)
-#define KVSEL_ATTN_G(D, F32) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, KVSEL_ATTN_KT, 4, true>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part, ga)
+#define KVSEL_ATTN(D, F32, W) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, KVSEL_ATTN_KT, W, false>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part, ga, cu_pair)
+#define KVSEL_ATTN_G(D, F32) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, KVSEL_ATTN_KT, 4, true>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part, ga, 0)
 #define KVSEL_ATTN_PPK(D, F32) hipLaunchKernelGGL((attn_pp_kernel<D, F32>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part)
         if (gather) {
             if (s.d == 128) { if (out_f32) KVSEL_ATTN_G(128, true); else KVSEL_ATTN_G(128, false); }

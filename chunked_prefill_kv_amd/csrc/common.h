@@ -100,10 +100,10 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // The 8 workgroup-dispatch queues of MI355X place consecutive workgroup ids on
 // consecutive XCDs (each with its own L2).  remap so that the workgroups one
 // XCD receives are consecutive slots (sharing the same head's data).
+constexpr int kXcds = 8;   // MI355X: 8 XCDs, workgroups dealt to them round-robin
 __device__ __forceinline__ int xcd_slot(int linear, int n) {
-    constexpr int kXcd = 8;
-    if (n % kXcd != 0) return linear;
-    return (linear % kXcd) * (n / kXcd) + linear / kXcd;
+    if (n % kXcds != 0) return linear;
+    return (linear % kXcds) * (n / kXcds) + linear / kXcds;
 }
 
 }  // namespace kvsel
