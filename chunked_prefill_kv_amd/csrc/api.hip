@@ -69,8 +69,11 @@ struct Trace {
     std::vector<hipEvent_t> pool;
     hipEvent_t take() {
         if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
+        // timing only, read after the caller's synchronisation: no system-scope
+        // fence (its cache writeback and invalidation would slow the launches
+        // being timed)
         hipEvent_t e = nullptr;
-        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
         return e;
     }
 };
