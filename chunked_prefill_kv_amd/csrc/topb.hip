@@ -115,6 +115,20 @@ __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
     __shared__ uint32_t sgt[1024], seq_[1024];      // per-segment counts (nseg <= 1024)
     __shared__ uint32_t wsum[16];
     __shared__ uint32_t s_bin, s_need, s_cnt, s_digit, s_rem;
+    const float* c = a.comb + static_cast<int64_t>(p) * a.s_stride;
+    // the pass's first scores are requested before the histogram, so they
+    // arrive while the boundary bin is found; each later step's scores are
+    // requested one step ahead (wave w reads [base0 + 512 w, +512) in 8
+    // loads of 64)
+    float v[8];
+    auto load_step = [&](int base0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = base0 + wave * 512 + i * kWave + lane;
+            v[i] = c[j < T ? j : T - 1];
+        }
+    };
+    load_step(0);
     const uint32_t* h = a.hist + static_cast<int64_t>(p) * kBins;
     for (int i = tid; i < kBins; i += 1024) hs[i] = h[i];
     for (int i = tid; i < a.nseg; i += 1024) { sgt[i] = 0; seq_[i] = 0; }
@@ -137,7 +151,6 @@ __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
     __syncthreads();
     const int bstar = static_cast<int>(s_bin);
     const uint32_t need = s_need;                 // keys kept from the boundary bin
-    const float* c = a.comb + static_cast<int64_t>(p) * a.s_stride;
     // one pass: keys above the boundary bin are counted per segment, boundary
     // keys collected.  Wave w takes keys [base0 + 512 w, +512) in 8 steps of
     // 64 (one segment: the count stays in a register, one LDS atomic per wave
@@ -145,17 +158,15 @@ __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
     const uint64_t lt = (1ull << lane) - 1ull;
     for (int base0 = 0; base0 < T; base0 += 8 * 1024) {
         const int wbase = base0 + wave * 512;
-        float v[8];
+        float cur[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {                  // 8 loads in flight per thread
-            const int j = wbase + i * kWave + lane;
-            v[i] = j < T ? c[j] : -2.0f;
-        }
+        for (int i = 0; i < 8; ++i) cur[i] = v[i];
+        if (base0 + 8 * 1024 < T) load_step(base0 + 8 * 1024);
         uint32_t ngt = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int j = wbase + i * kWave + lane;
-            const int bn = j < T ? value_bin(v[i]) : -1;
+            const int bn = j < T ? value_bin(cur[i]) : -1;
             ngt += static_cast<uint32_t>(__popcll(__ballot(bn > bstar)));
             const uint64_t beq = __ballot(bn == bstar);
             if (beq) {
@@ -164,7 +175,7 @@ __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
                 first = __shfl(first, 0, kWave);
                 if (bn == bstar) {
                     const uint32_t pos = first + static_cast<uint32_t>(__popcll(beq & lt));
-                    if (pos < kCap) { ck[pos] = order_key(v[i]); cj[pos] = j; }
+                    if (pos < kCap) { ck[pos] = order_key(cur[i]); cj[pos] = j; }
                 }
             }
         }
@@ -257,6 +268,17 @@ __global__ __launch_bounds__(256) void topb_write_kernel(TopbArgs a) {
     }
     const int T = static_cast<int>(T64);
     if (j0 >= T) return;
+    // wave w owns keys [j0 + 512 w, j0 + 512 (w + 1)) in 8 steps of 64; the
+    // scores are requested first (unconditionally, past T the last key), so
+    // they arrive while the threshold and the earlier segments' counts load
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const float* c = a.comb + static_cast<int64_t>(p) * a.s_stride;
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int j = j0 + wave * 512 + i * kWave + lane;
+        sv[i] = c[j < T ? j : T - 1];
+    }
     const uint32_t tau = a.thr[2 * p], need_eq = a.thr[2 * p + 1];
     const uint32_t* sc = a.segc + static_cast<int64_t>(p) * a.nseg * 2;
     __shared__ uint32_t wcnt[2][4];
@@ -267,16 +289,12 @@ __global__ __launch_bounds__(256) void topb_write_kernel(TopbArgs a) {
         base_gt = g;
         base_eq = e;
     }
-    // wave w owns keys [j0 + 512 w, j0 + 512 (w + 1)) in 8 steps of 64
-    const int lane = lane_id(), wave = threadIdx.x / kWave;
-    const float* c = a.comb + static_cast<int64_t>(p) * a.s_stride;
     uint32_t u[8];
     bool in[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int j = j0 + wave * 512 + i * kWave + lane;
-        in[i] = j < T;
-        u[i] = in[i] ? order_key(c[j]) : 0u;
+        in[i] = j0 + wave * 512 + i * kWave + lane < T;
+        u[i] = in[i] ? order_key(sv[i]) : 0u;
     }
     uint32_t ng = 0, ne = 0;
 #pragma unroll
