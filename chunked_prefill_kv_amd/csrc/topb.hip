@@ -50,20 +50,22 @@ struct TopbArgs {
 
 __global__ __launch_bounds__(256) void topb_hist_kernel(TopbArgs a) {
     const int p = blockIdx.x / a.nseg, seg = blockIdx.x % a.nseg;
-    const int64_t T = a.prior_len[p / a.heads_per_seq];
-    if (T <= a.budget) return;
     const int j0 = seg * kSeg;
-    if (j0 >= T) return;
-    __shared__ uint32_t lh[kBins];
-    for (int i = threadIdx.x; i < kBins; i += 256) lh[i] = 0;
-    __syncthreads();
+    // the first split's scores are requested before the prior length is known
+    // (inside the problem's row of s_stride entries; keys past T are dropped)
     const float* x = a.part + static_cast<int64_t>(p) * a.s_stride;
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int j = j0 + i * 256 + threadIdx.x;
-        v[i] = j < T ? x[j] : 0.0f;
+        const int64_t j = j0 + i * 256 + threadIdx.x;
+        v[i] = x[j < a.s_stride ? j : a.s_stride - 1];
     }
+    const int64_t T = a.prior_len[p / a.heads_per_seq];
+    if (T <= a.budget) return;
+    if (j0 >= T) return;
+    __shared__ uint32_t lh[kBins];
+    for (int i = threadIdx.x; i < kBins; i += 256) lh[i] = 0;
+    __syncthreads();
     for (int sp = 1; sp < a.nsplit; ++sp) {          // partials added in split order
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -253,6 +255,18 @@ __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
 
 __global__ __launch_bounds__(256) void topb_write_kernel(TopbArgs a) {
     const int p = blockIdx.x / a.nseg, seg = blockIdx.x % a.nseg;
+    // wave w owns keys [j0 + 512 w, j0 + 512 (w + 1)) in 8 steps of 64; the
+    // scores are requested first, before the prior length, the threshold and
+    // the earlier segments' counts (inside the problem's row of s_stride
+    // entries; keys past T are not used)
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const float* c = a.comb + static_cast<int64_t>(p) * a.s_stride;
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t j = seg * kSeg + wave * 512 + i * kWave + lane;
+        sv[i] = c[j < a.s_stride ? j : a.s_stride - 1];
+    }
     const int64_t T64 = a.prior_len[p / a.heads_per_seq];
     int32_t* o = a.out + static_cast<int64_t>(p) * a.budget;
     const int j0 = seg * kSeg;
@@ -268,17 +282,6 @@ __global__ __launch_bounds__(256) void topb_write_kernel(TopbArgs a) {
     }
     const int T = static_cast<int>(T64);
     if (j0 >= T) return;
-    // wave w owns keys [j0 + 512 w, j0 + 512 (w + 1)) in 8 steps of 64; the
-    // scores are requested first (unconditionally, past T the last key), so
-    // they arrive while the threshold and the earlier segments' counts load
-    const int lane = lane_id(), wave = threadIdx.x / kWave;
-    const float* c = a.comb + static_cast<int64_t>(p) * a.s_stride;
-    float sv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int j = j0 + wave * 512 + i * kWave + lane;
-        sv[i] = c[j < T ? j : T - 1];
-    }
     const uint32_t tau = a.thr[2 * p], need_eq = a.thr[2 * p + 1];
     const uint32_t* sc = a.segc + static_cast<int64_t>(p) * a.nseg * 2;
     __shared__ uint32_t wcnt[2][4];
