@@ -50,7 +50,6 @@ __global__ __launch_bounds__(256) void qsum_kernel(const T* __restrict__ q, int 
     constexpr int RPP = 256 / G8;             // rows per pass
     for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < zero_n; i += int64_t(gridDim.x) * 256) zero[i] = 0;
     const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
-    if (prior_len[bh / h_q] <= budget) return;
     const T* qh = q + static_cast<int64_t>(bh) * C * D;
     const int c8 = threadIdx.x % G8, sub = threadIdx.x / G8;
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -58,11 +57,12 @@ __global__ __launch_bounds__(256) void qsum_kernel(const T* __restrict__ q, int 
     constexpr int NIT = QR / RPP;
     float x[NIT][8];
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {           // all loads in flight first
+    for (int it = 0; it < NIT; ++it) {           // all loads in flight first, before the prior length
         const int r = blk * QR + sub + it * RPP;
         if (r < r1) Vec8<T>::load(qh + static_cast<int64_t>(r) * D + c8 * 8, x[it]);
         else for (int i = 0; i < 8; ++i) x[it][i] = 0.0f;
     }
+    if (prior_len[bh / h_q] <= budget) return;
 #pragma unroll
     for (int it = 0; it < NIT; ++it)
 #pragma unroll
@@ -87,8 +87,8 @@ __global__ __launch_bounds__(256) void qcos_kernel(const T* __restrict__ q, int 
     constexpr int G8 = D / 8;
     constexpr int RPP = 256 / G8;
     const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
-    if (prior_len[bh / h_q] <= budget) return;
-    // this block's query rows are loaded first, so they arrive while the mean is formed
+    // this block's query rows are loaded first (before the prior length), so
+    // they arrive while the mean is formed
     const int c8 = threadIdx.x % G8, sub = threadIdx.x / G8;
     const T* qh = q + static_cast<int64_t>(bh) * C * D;
     const int r1 = min(C, (blk + 1) * QR);
@@ -100,6 +100,7 @@ __global__ __launch_bounds__(256) void qcos_kernel(const T* __restrict__ q, int 
         if (r < r1) Vec8<T>::load(qh + static_cast<int64_t>(r) * D + c8 * 8, x[it]);
         else for (int i = 0; i < 8; ++i) x[it][i] = 0.0f;
     }
+    if (prior_len[bh / h_q] <= budget) return;
     __shared__ double mean[D];
     __shared__ double mnorm;
     {
@@ -375,22 +376,29 @@ __global__ __launch_bounds__(256) void pack_qsel_kernel(const T* __restrict__ q,
     for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < zero_n; i += int64_t(gridDim.x) * 256) zero[i] = 0;
     const int bh = blockIdx.x / rblocks, rb = blockIdx.x % rblocks;
     const int b = bh / h_q, h = bh % h_q;
-    if (prior_len[b] <= budget) return;
     const int g = h / G, hh = h % G;
     const int h_kv = h_q / G;
     const int64_t dst_row0 = (static_cast<int64_t>(b) * h_kv + g) * G * nq_pad + static_cast<int64_t>(hh) * nq_pad;
     int32_t* kp = keep + static_cast<int64_t>(bh) * keep_stride;
     // kept token of row r (rows past nqp repeat row 0); with every query kept
-    // (nqp == C) the list is the identity and the statistics were not run
+    // (nqp == C) the list is the identity and the statistics were not run.
+    // The list entries are read before the prior length (the list is written
+    // only for selecting sequences, so the rows themselves are read after).
     auto kept = [&](int r) { return keep_all ? (r < nqp ? r : 0) : kp[r < nqp ? r : 0]; };
-    u32x4 v[PPT];
-    int rr[PPT];
+    int rr[PPT], tk[PPT];
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
         const int p = threadIdx.x + 256 * i;
-        const int r = rb * kRows + p / kPieces, pc = p % kPieces;
-        rr[i] = r;
-        if (r < nq_pad) v[i] = reinterpret_cast<const u32x4*>(q + (static_cast<int64_t>(bh) * C + kept(r)) * D)[pc];
+        rr[i] = rb * kRows + p / kPieces;
+        tk[i] = rr[i] < nq_pad ? kept(rr[i]) : 0;
+    }
+    if (prior_len[b] <= budget) return;
+    u32x4 v[PPT];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int p = threadIdx.x + 256 * i;
+        const int r = rr[i], pc = p % kPieces;
+        if (r < nq_pad) v[i] = reinterpret_cast<const u32x4*>(q + (static_cast<int64_t>(bh) * C + tk[i]) * D)[pc];
     }
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
