@@ -137,19 +137,21 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
     const int hh = rvalid ? qrow % G : 0;
     const int64_t qoff = ((static_cast<int64_t>(b) * h_kv * G + g * G + hh) * C + tok) * D;
 
+    // (a lane past the last row reads the head's first row: qoff points there)
     bf16x8 qf[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (rvalid) raw = *reinterpret_cast<const u32x4*>(q + qoff + 16 * ks + 8 * half);
-        qf[ks] = __builtin_bit_cast(bf16x8, raw);
-    }
-    // Complete the Q loads here, on every path: otherwise the loop header
-    // merges a path on which they may still be in flight and the compiler's
-    // wait analysis puts a wait for every outstanding load (including the
-    // next tile's, just issued) in front of each tile's first MFMA.
+    for (int ks = 0; ks < KS; ++ks)
+        qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + qoff + 16 * ks + 8 * half));
+    // The Q loads are completed before the tile loop, on every path: otherwise
+    // the loop header merges a path on which they may still be in flight and
+    // the compiler's wait analysis puts a wait for every outstanding load
+    // (including the next tile's, just issued) in front of each tile's first
+    // MFMA.  The packed path completes them after requesting its first tile.
+    auto complete_q = [&] {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+    };
+    if constexpr (GATHER) complete_q();
 
     const uint16_t* kb = kall + static_cast<int64_t>(bg) * nk_pad * D;
     const uint16_t* vb = vall + static_cast<int64_t>(bg) * D * nk_pad;
@@ -381,8 +383,11 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
         if (ntiles > 0) {
             fetch_k(tix(0));
             fetch_v(tix(0));
+            complete_q();
             stash_k(0);
             stash_v(0);
+        } else {
+            complete_q();
         }
         fetch_k(tix(1));
     }
