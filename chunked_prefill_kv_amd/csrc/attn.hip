@@ -524,15 +524,16 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(const uint16_t* __restr
     const int hh = rvalid ? qrow % G : 0;
     const int64_t qoff = ((static_cast<int64_t>(b) * h_kv * G + g * G + hh) * C + tok) * D;
 
+    // (a lane past the last row reads the head's first row: qoff points there);
+    // the loads are completed after the first tile is requested (prologue)
     bf16x8 qf[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (rvalid) raw = *reinterpret_cast<const u32x4*>(q + qoff + 16 * ks + 8 * half);
-        qf[ks] = __builtin_bit_cast(bf16x8, raw);
-    }
+    for (int ks = 0; ks < KS; ++ks)
+        qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + qoff + 16 * ks + 8 * half));
+    auto complete_q = [&] {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+    };
 
     const uint16_t* kb = kall + static_cast<int64_t>(bg) * nk_pad * D;
     const uint16_t* vb = vall + static_cast<int64_t>(bg) * D * nk_pad;
@@ -693,10 +694,13 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(const uint16_t* __restr
     if (ntiles > 0) {
         fetch(0, tix(0), tix(0));
         fetch(1, tix(0), tix(0));
+        complete_q();
         stash(0, 0, 0);
         stash(1, 0, 0);                      // V(0) also lands in stage 0 here (rewritten below)
         fetch(0, tix(1), tix(0));
         fetch(1, tix(1), tix(0));
+    } else {
+        complete_q();
     }
     __syncthreads();
     if (ntiles > 0 && grp == 1) {            // group B: the second half of the interval before the loop
