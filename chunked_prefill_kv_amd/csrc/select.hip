@@ -214,18 +214,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     const int p = blockIdx.x;
     const int b = p / heads_per_seq;
     const int64_t T = prior_len[b];
-    int n;
-    if (mode == 0) {
-        n = static_cast<int>(T);
-    } else {
-        if (T <= budget) return;
-        n = n_fixed;
-    }
+    // mode 1: the problem size does not depend on T, so the keys are requested
+    // before T is checked (sequences with T <= budget return after the first pass)
+    const int n = mode == 0 ? static_cast<int>(T) : n_fixed;
     const float* x = scores + static_cast<int64_t>(p) * score_stride;
     int32_t* o = out + static_cast<int64_t>(p) * out_stride;
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
 
     if (n <= k) {   // everything is kept
+        if (mode == 1 && T <= budget) return;
         for (int j = tid; j < k; j += kTopkThreads) o[j] = j < n ? j : -1;
         return;
     }
@@ -264,6 +261,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
             diff |= u ^ first;
         }
     }
+    if (mode == 1 && T <= budget) return;             // the whole workgroup: before any barrier
 #pragma unroll
     for (int o2 = 32; o2 >= 1; o2 >>= 1) diff |= __shfl_xor(diff, o2, kWave);
     if (lane == 0) wsum[wave] = diff;
