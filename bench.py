@@ -126,7 +126,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the kernels shard by KV head "
-              f"with no exchange, but multi-GPU runs are not part of this build", file=sys.stderr)
+              f"with no exchange, and multi-GPU execution is not implemented", file=sys.stderr)
         sys.exit(2)
 
     import torch

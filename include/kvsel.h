@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
     KVSEL_OK = 0,
     KVSEL_ERR_INVALID_ARG = 1,   /* a null pointer, a bad shape, an out-of-range value */
-    KVSEL_ERR_UNSUPPORTED = 2,   /* a valid request this build does not implement (e.g. d = 96) */
+    KVSEL_ERR_UNSUPPORTED = 2,   /* a valid request the library does not implement (e.g. d = 96) */
     KVSEL_ERR_WORKSPACE = 3,     /* workspace missing or smaller than kvsel_workspace_size() */
     KVSEL_ERR_HIP = 4            /* a HIP launch failed; kvsel_last_error() has the HIP message */
 } kvsel_status;
