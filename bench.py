@@ -12,7 +12,9 @@ in HBM before timing starts.  Prints one JSON line:
              launch / its average launch time, against bf16 dense MFMA peak;
              launch times come from HIP events recorded on the launch stream
              (kvsel_trace_*) over a second pass of the same K steps
-  cpu_baseline  the CPU oracle timed on this host on a bounded sample
+  cpu_baseline  the CPU oracle timed on this host on the same inputs (the
+             whole prompt of the 32K layer; the whole decode step), with the
+             threads it may use and the CPU model
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -86,33 +88,67 @@ def algorithmic_work(wl, starts, lens, pooling="head"):
     return att_flop, att_bytes, scan_flop, scan_bytes
 
 
-def cpu_baseline(wl, chunks, sample_every=None, pooling="head"):
-    """The oracle, as it stands, on every `sample_every`-th chunk (the last of each group);
-    by default every 4th chunk of prompts of up to 16 chunks (about 10 s of host work at
-    32K tokens), else every 8th."""
-    if sample_every is None:
-        sample_every = 4 if len(chunks) <= 16 else 8
+def host_cpu():
+    """(threads this process may run on, CPU model name) of the host."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return cores, model
+
+
+def cpu_baseline(wl, chunks, pooling="head"):
+    """The oracle, as it stands, on the same inputs: the whole prompt for prompts of
+    up to 16 chunks (the 32K layer: about 40 s of host work), else every 8th chunk
+    (the last of each group of 8) over the full prior cache."""
     from chunked_prefill_kv_amd import gen
     from oracle import quoka
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
-    ks = list(range(sample_every - 1, len(chunks), sample_every))
-    tokens = 0
-    t_total = 0.0
-    for k in ks:
-        Qc, Kc, Vc = (gen.to_f64(x) for x in chunks[k])
-        Kp = np.concatenate([gen.to_f64(c[1]) for c in chunks[:k]], axis=1)
-        Vp = np.concatenate([gen.to_f64(c[2]) for c in chunks[:k]], axis=1)
+    cores, model = host_cpu()
+    c64 = [tuple(gen.to_f64(x) for x in c) for c in chunks]
+    if len(chunks) <= 16:
         t0 = time.perf_counter()
-        quoka.prefill_chunk(Qc, Kc, Vc, Kp, Vp, wl.n_q, wl.B, pooling=pooling)
-        t_total += time.perf_counter() - t0
-        tokens += Qc.shape[1]
+        quoka.prefill(c64, wl.n_q, wl.B, pooling=pooling)
+        t_total = time.perf_counter() - t0
+        tokens = sum(c[0].shape[1] for c in c64)
+        what = f"the whole {len(chunks)}-chunk prompt"
+    else:
+        ks = list(range(7, len(chunks), 8))
+        tokens, t_total = 0, 0.0
+        for k in ks:
+            Qc, Kc, Vc = c64[k]
+            Kp = np.concatenate([c[1] for c in c64[:k]], axis=1)
+            Vp = np.concatenate([c[2] for c in c64[:k]], axis=1)
+            t0 = time.perf_counter()
+            quoka.prefill_chunk(Qc, Kc, Vc, Kp, Vp, wl.n_q, wl.B, pooling=pooling)
+            t_total += time.perf_counter() - t0
+            tokens += Qc.shape[1]
+        what = f"chunks {ks} of the {len(chunks)}-chunk prompt"
     return {"value": tokens / t_total, "unit": "tokens/s/layer", "cores": cores, "kind": "oracle",
-            "sample": f"chunks {ks} of the {len(chunks)}-chunk prompt (all heads, fp64 numpy), "
-                      f"{tokens} tokens in {t_total:.1f} s"}
+            "cpu": model,
+            "sample": f"{what} (all heads, fp64 numpy), {tokens} tokens in {t_total:.1f} s"}
+
+
+def cpu_baseline_decode(wl, di):
+    """The oracle on the whole ragged decode step (every sequence: select over its
+    prior cache, attend), inputs read back from the paged pool beforehand."""
+    from chunked_prefill_kv_amd import gen
+    from oracle import quoka
+    cores, model = host_cpu()
+    t_total = 0.0
+    for b in range(wl.batch):
+        kp, vp = di.logical_kv(b, wl.block_size)
+        Kp, Vp, Qc = gen.to_f64(kp), gen.to_f64(vp), gen.to_f64(di.q[b])
+        Kn, Vn = gen.to_f64(di.k_new[b]), gen.to_f64(di.v_new[b])
+        t0 = time.perf_counter()
+        quoka.prefill_chunk(Qc, Kn, Vn, Kp, Vp, wl.n_q, wl.B)
+        t_total += time.perf_counter() - t0
+    return {"value": wl.batch / t_total, "unit": "tokens/s/layer", "cores": cores, "kind": "oracle", "cpu": model,
+            "sample": f"the whole decode step ({wl.batch} sequences, all heads, fp64 numpy) in {t_total:.1f} s"}
 
 
 def main():
@@ -226,7 +262,7 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, chunks, pooling=args.pooling)
     else:
         out["cpu_baseline"] = None
@@ -278,6 +314,9 @@ def bench_decode(args):
                         "launches": n_sc, "avg_launch_us": round(ms_sc * 1e3 / n_sc, 2)},
            "kernels": {k: {"ms_per_step": round(v[1] / args.steps, 4)} for k, v in tr.items()},
            "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on the decode step", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_decode(wl, di)
     print(json.dumps(out), flush=True)
 
 

@@ -140,6 +140,15 @@ kvsel_status check_params(const kvsel_params* p) {
     return KVSEL_OK;
 }
 
+// Selection limits: the top-B's per-segment counters (kTopbMaxSegments
+// segments of kTopbSegKeys keys) bound the prior length and the budget.
+kvsel_status check_select(int64_t t_max, const kvsel_params* p) {
+    if (topb_segments(t_max, p->budget) > kTopbMaxSegments)
+        return fail(KVSEL_ERR_UNSUPPORTED, "prior length %lld / budget %d: at most %lld keys per sequence can be selected from",
+                    (long long)t_max, p->budget, (long long)kTopbSegKeys * kTopbMaxSegments);
+    return KVSEL_OK;
+}
+
 // extra = rows past T_b that the call writes (chunk_len for prefill, 0 for select)
 kvsel_status check_cache(const kvsel_cache* c, const kvsel_batch* b, int extra) {
     if (!c) return fail(KVSEL_ERR_INVALID_ARG, "cache is NULL");
@@ -257,6 +266,12 @@ Layout layout(const SelShape& s, bool with_attn) {
     return L;
 }
 
+// Whether kvsel_prefill_chunk takes the gathering attention (kept rows read in
+// place through their cache row numbers, no packed lists) for these shapes.
+bool prefill_uses_gather(const SelShape& s, const kvsel_cache* c, const kvsel_heads* h, const kvsel_batch* b) {
+    return attn_use_gather(s) && cache_rows_fit(c, h, b);
+}
+
 template <typename P> P* at(void* ws, size_t off) { return reinterpret_cast<P*>(static_cast<char*>(ws) + off); }
 
 kvsel_status check_ws(void* ws, size_t have, size_t need) {
@@ -352,16 +367,39 @@ kvsel_status kvsel_trace_read(int32_t* launches, float* total_ms, int32_t n) {
 
 const char* kvsel_kernel_name(int32_t id) { return (id >= 0 && id < KVSEL_K_COUNT) ? kKernelNames[id] : ""; }
 
-int32_t kvsel_version(void) { return 101; }
+int32_t kvsel_version(void) { return 102; }
 
 kvsel_status kvsel_workspace_size(const kvsel_heads* heads, const kvsel_batch* batch, const kvsel_params* params,
                                   size_t* bytes) {
     g_err.clear();
     kvsel_status st;
     int64_t t_max;
-    if ((st = check_heads(heads)) || (st = check_batch(batch, true, &t_max)) || (st = check_params(params))) return st;
+    if ((st = check_heads(heads)) || (st = check_batch(batch, true, &t_max)) || (st = check_params(params)) ||
+        (st = check_select(t_max, params)))
+        return st;
     if (!bytes) return fail(KVSEL_ERR_INVALID_ARG, "bytes is NULL");
     *bytes = layout(make_shape(heads, batch, params, t_max), true).total;
+    return KVSEL_OK;
+}
+
+kvsel_status kvsel_compacted_view(const kvsel_heads* heads, const kvsel_batch* batch, const kvsel_params* params,
+                                  const kvsel_cache* cache, int32_t* packed, size_t* k_offset, size_t* v_offset,
+                                  int32_t* slots, int32_t* v_transposed) {
+    g_err.clear();
+    kvsel_status st;
+    int64_t t_max;
+    if ((st = check_heads(heads)) || (st = check_batch(batch, true, &t_max)) || (st = check_params(params)) ||
+        (st = check_select(t_max, params)) || (st = check_cache(cache, batch, batch->chunk_len)))
+        return st;
+    if (!packed || !k_offset || !v_offset || !slots || !v_transposed)
+        return fail(KVSEL_ERR_INVALID_ARG, "an output pointer is NULL");
+    const SelShape s = make_shape(heads, batch, params, t_max);
+    const Layout L = layout(s, true);
+    *packed = prefill_uses_gather(s, cache, heads, batch) ? 0 : 1;
+    *k_offset = L.kall;
+    *v_offset = L.vall;
+    *slots = L.nk_pad;
+    *v_transposed = s.esz == 2 ? 1 : 0;
     return KVSEL_OK;
 }
 
@@ -387,7 +425,7 @@ kvsel_status kvsel_select(const kvsel_heads* heads, const kvsel_batch* batch, co
     kvsel_status st;
     int64_t t_max;
     if ((st = check_heads(heads)) || (st = check_batch(batch, true, &t_max)) || (st = check_params(params)) ||
-        (st = check_cache(cache, batch, 0)))
+        (st = check_select(t_max, params)) || (st = check_cache(cache, batch, 0)))
         return st;
     if (!q || !aligned16(q)) return fail(KVSEL_ERR_INVALID_ARG, "q is NULL or not 16-byte aligned");
     if (!idx) return fail(KVSEL_ERR_INVALID_ARG, "idx is NULL");
@@ -447,7 +485,7 @@ kvsel_status kvsel_prefill_chunk(const kvsel_heads* heads, const kvsel_batch* ba
     kvsel_status st;
     int64_t t_max;
     if ((st = check_heads(heads)) || (st = check_batch(batch, true, &t_max)) || (st = check_params(params)) ||
-        (st = check_cache(cache, batch, batch->chunk_len)))
+        (st = check_select(t_max, params)) || (st = check_cache(cache, batch, batch->chunk_len)))
         return st;
     if (!q || !k_chunk || !v_chunk || !out) return fail(KVSEL_ERR_INVALID_ARG, "q/k_chunk/v_chunk/out is NULL");
     if (!aligned16(q) || !aligned16(k_chunk) || !aligned16(v_chunk) || !aligned16(out))
@@ -459,7 +497,7 @@ kvsel_status kvsel_prefill_chunk(const kvsel_heads* heads, const kvsel_batch* ba
     const CacheView cv = make_view(cache, heads);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     int32_t* idx_buf = idx ? idx : at<int32_t>(workspace, L.idx);
-    const bool gather = attn_use_gather(s) && cache_rows_fit(cache, heads, batch);
+    const bool gather = prefill_uses_gather(s, cache, heads, batch);
     int32_t* rowidx = gather ? at<int32_t>(workspace, L.rowidx) : nullptr;
     if ((st = run_select(s, batch, q, cv, workspace, L, idx_buf, nullptr, nullptr, hs, rowidx))) return st;
     PackSrc src{};

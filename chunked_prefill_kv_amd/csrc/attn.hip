@@ -46,22 +46,10 @@ __device__ __forceinline__ int sigma(int m) {
 // Per 64-key tile: S^T = K . Q^T (2 x KS MFMAs), online softmax on the lane's
 // query column, O^T += V^T . P^T (DB x 4 MFMAs).  K tiles are row-major
 // [key][d] and V tiles are [d][key] (written transposed by the pack kernel).
-#ifndef KVSEL_ATTN_KT
-#define KVSEL_ATTN_KT 64
-#endif
-#ifndef KVSEL_ATTN_PRIO
-#define KVSEL_ATTN_PRIO 1
-#endif
-#define KVSEL_SETPRIO(p) do { if (KVSEL_ATTN_PRIO) __builtin_amdgcn_s_setprio(p); } while (0)
-#ifndef KVSEL_ATTN_GATHER
-#define KVSEL_ATTN_GATHER 1               // gathering attention for single-row-block KV heads
-#endif
-#ifndef KVSEL_ATTN_PP
-#define KVSEL_ATTN_PP 1                   // packed path: ping-pong kernel (8 waves, 256 rows)
-#endif
-#ifndef KVSEL_ATTN_CU_PAIR
-#define KVSEL_ATTN_CU_PAIR 1              // one-round 4-wave grids: long and short row blocks share a CU
-#endif
+constexpr int kAttnKT = 64;           // keys per staged tile
+// wave priority: MFMA issue runs at priority 1, the softmax at 0 (it yields
+// the issue slot to the other wave of the SIMD)
+#define KVSEL_SETPRIO(p) __builtin_amdgcn_s_setprio(p)
 
 //
 // GATHER: the key list is read from its sources (kept cache rows through idx,
@@ -867,7 +855,7 @@ __global__ __launch_bounds__(128) void attn_valu_kernel(const float* __restrict_
 
 // ----------------------------------------------------------------------------- launcher
 
-bool attn_use_gather(const SelShape& s) { return KVSEL_ATTN_GATHER && s.esz == 2 && s.G * s.C <= 128; }
+bool attn_use_gather(const SelShape& s) { return s.esz == 2 && s.G * s.C <= 128; }
 // Ping-pong kernel: packed bf16 path with d = 128 (two staged pieces per
 // thread), where its 256-row grid either splits keys (fewer workgroups than
 // CUs) or holds two or more workgroups per CU.  In between (one round of one
@@ -875,7 +863,7 @@ bool attn_use_gather(const SelShape& s) { return KVSEL_ATTN_GATHER && s.esz == 2
 // row blocks); with splits and with several rounds the ping-pong kernel was
 // 1.7-3% faster.
 static bool attn_use_pp(const SelShape& s) {
-    if (!(KVSEL_ATTN_PP && s.esz == 2 && s.d == 128 && !attn_use_gather(s))) return false;
+    if (!(s.esz == 2 && s.d == 128 && !attn_use_gather(s))) return false;
     const int64_t wgs = int64_t(s.batch) * s.h_kv * ((s.G * s.C + 255) / 256);
     return wgs < 256 || wgs >= 512;
 }
@@ -912,14 +900,14 @@ hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const
         // 4-wave packed kernel in one round of two workgroups per CU, whole KV
         // heads per XCD: pair long with short row blocks on each CU
         const int64_t per_xcd = grid.x / kXcds;
-        const int cu_pair = (KVSEL_ATTN_CU_PAIR && !gather && !pp && ksplit == 1 && row_blocks > 1 &&
+        const int cu_pair = (!gather && !pp && ksplit == 1 && row_blocks > 1 &&
                              grid.x % kXcds == 0 && per_xcd % row_blocks == 0 &&
                              int64_t(grid.x) <= 2 * int64_t(device_cus())) ? 1 : 0;
         const float cl2 = scale * 1.4426950408889634f;
         const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)kall, *vv = (const uint16_t*)vall;
         const AttnGather ga = gather ? *gather : AttnGather{};
-#define KVSEL_ATTN(D, F32, W) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, KVSEL_ATTN_KT, W, false>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part, ga, cu_pair)
-#define KVSEL_ATTN_G(D, F32) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, KVSEL_ATTN_KT, 4, true>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part, ga, 0)
+#define KVSEL_ATTN(D, F32, W) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, kAttnKT, W, false>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part, ga, cu_pair)
+#define KVSEL_ATTN_G(D, F32) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, kAttnKT, 4, true>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part, ga, 0)
 #define KVSEL_ATTN_PPK(D, F32) hipLaunchKernelGGL((attn_pp_kernel<D, F32>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part)
         if (gather) {
             if (s.d == 128) { if (out_f32) KVSEL_ATTN_G(128, true); else KVSEL_ATTN_G(128, false); }

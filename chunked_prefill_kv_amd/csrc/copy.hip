@@ -25,6 +25,7 @@ struct PackArgs {
     const char* v_compact;
     const int32_t* n_sel;
     int n_sel_max;
+    bool compact;            // prior keys from k_compact / v_compact (else from the cache through idx)
     const char* k_chunk;
     const char* v_chunk;
     int C, h_kv, nk_pad, tiles, row_bytes;
@@ -39,7 +40,7 @@ __device__ __forceinline__ void slot_source(const PackArgs& a, int b, int g, int
                                             const char** kp, const char** vp) {
     const int64_t bg = static_cast<int64_t>(b) * a.h_kv + g;
     if (s < nsel_b) {
-        if (a.k_compact) {
+        if (a.compact) {
             const int64_t off = (bg * a.n_sel_max + s) * a.row_bytes;
             *kp = a.k_compact + off;
             *vp = a.v_compact + off;
@@ -60,7 +61,7 @@ __device__ __forceinline__ void slot_source(const PackArgs& a, int b, int g, int
 }
 
 __device__ __forceinline__ int seq_nsel(const PackArgs& a, int b, int64_t* T) {
-    if (a.k_compact) {           // caller-supplied count, clamped to the array it indexes
+    if (a.compact) {             // caller-supplied count, clamped to the array it indexes
         *T = 0;
         const int v = a.n_sel[b];
         return v < 0 ? 0 : (v > a.n_sel_max ? a.n_sel_max : v);
@@ -213,6 +214,7 @@ hipError_t launch_pack(const SelShape& s, const PackSrc& src, const void* k_chun
     a.v_compact = static_cast<const char*>(src.v_compact);
     a.n_sel = src.n_sel;
     a.n_sel_max = src.n_sel_max;
+    a.compact = src.cache == nullptr;    // no cache given: the caller's compacted arrays (possibly empty)
     a.k_chunk = static_cast<const char*>(k_chunk);
     a.v_chunk = static_cast<const char*>(v_chunk);
     a.C = s.C;

@@ -23,13 +23,9 @@ struct SelShape {
 
 // Choose how many query-head groups the MFMA scan splits a KV head into: a
 // power of two dividing G (at most 8), the smallest that gives >= 512
-// workgroups for the largest prior length.
-#ifndef KVSEL_SCAN_NB
-#define KVSEL_SCAN_NB 3
-#endif
-constexpr int kScanNB = KVSEL_SCAN_NB;   // 32-key blocks per wave of the prefill scan (4 waves)
-// (counted in 256-key tiles whatever kScanNB is: every split adds a pass of
-// the top-B over the scores, so the split count is not raised with the tile)
+// workgroups for the largest prior length (counted in 256-key tiles whatever
+// the scan's per-launch tile is: every split adds a pass of the top-B over the
+// scores, so the split count is not raised with the tile).
 inline int scan_splits(int batch, int h_kv, int G, int64_t t_max) {
     const int64_t tiles = (t_max + 255) / 256;
     int ns = 1;
@@ -73,6 +69,10 @@ hipError_t launch_topk(int problems, int heads_per_seq, const float* scores, int
 // Compute units of the current device (queried once per device; 256 if the
 // query fails).  Launch shapes that run in rounds are sized with it.
 int device_cus();
+// The top-B counts kept keys per 2048-key segment in LDS, for at most
+// kTopbMaxSegments segments: max(T_max, budget) <= 2^21.
+constexpr int kTopbSegKeys = 2048;
+constexpr int kTopbMaxSegments = 1024;
 int topb_segments(int64_t t_max, int64_t budget);
 size_t topb_scratch_bytes(int problems, int64_t t_max, int64_t budget);
 hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int nsplit, int64_t split_stride,
@@ -117,13 +117,14 @@ hipError_t launch_gather(const SelShape& s, const CacheView& cv, const int64_t* 
 //   are also written into the cache (the prior rows it reads are [0, T_b), so
 //   the two never overlap).
 struct PackSrc {
-    // prior keys from the cache through idx (compact == nullptr) ...
+    // prior keys from the cache through idx (cache != nullptr) ...
     const CacheView* cache;
     const int64_t* prior_len;
     int64_t budget;
     const int32_t* idx;
     int64_t idx_stride;
-    // ... or from a caller-supplied compacted array [b][g][n_sel_max][d]
+    // ... or, with cache == nullptr, from a caller-supplied compacted array
+    // [b][g][n_sel_max][d] (k_compact / v_compact may be NULL when n_sel_max == 0)
     const void* k_compact;
     const void* v_compact;
     const int32_t* n_sel;

@@ -10,11 +10,9 @@
 // bf16); 1/|k_j| is common to every query so it is applied after the max.
 #include "launch.h"
 
-#ifndef KVSEL_ROWS16_GROUPS
-#define KVSEL_ROWS16_GROUPS 4   // 16-key groups per wave of the one-query scan
-#endif
-
 namespace kvsel {
+
+constexpr int kRows16Groups = 4;   // 16-key groups per wave of the one-query scan
 
 // ----------------------------------------------------------------------------- prefill scan (MFMA 32x32x16)
 //
@@ -34,17 +32,10 @@ namespace kvsel {
 // workgroups when the cache or the KV head count is small); split s writes
 // the sum over its heads, scaled by 1/G, to S + s * split_stride and the top-B
 // kernel adds the splits in order.
-#ifndef KVSEL_SCAN_NB4
-#define KVSEL_SCAN_NB4 1        // four 32-key blocks per wave where that fills the CUs best
-#endif
-#ifndef KVSEL_SCAN_W4
-#define KVSEL_SCAN_W4 0.78      // its time per key relative to two blocks
-#endif
-#ifndef KVSEL_SCAN_OCC
-#define KVSEL_SCAN_OCC 2        // workgroups per CU the register budget is sized for
-#endif
+constexpr double kScanW4 = 0.78;   // time per key of four 32-key blocks per wave, relative to two
+constexpr int kScanOcc = 2;        // workgroups per CU the register budget is sized for
 template <int D, int NB, int QK>
-__global__ __launch_bounds__(256, KVSEL_SCAN_OCC) void scan_mfma_kernel(const uint16_t* __restrict__ qsel,
+__global__ __launch_bounds__(256, kScanOcc) void scan_mfma_kernel(const uint16_t* __restrict__ qsel,
                                                            const float* __restrict__ rq, CacheView cv,
                                                            const int64_t* __restrict__ prior_len, int64_t budget,
                                                            int h_kv, int G, int nq_pad, int tiles, int nsplit,
@@ -348,7 +339,7 @@ hipError_t launch_scan(const SelShape& s, const void* qsel, const float* rq, con
                        const int64_t* prior_len, float* S, int64_t s_stride, hipStream_t st) {
     const int bgs = s.batch * s.h_kv;
     if (s.esz == 2 && s.nq_pad == 1 && !s.qsplit) {   // one query per head, G <= 16
-        constexpr int GR = KVSEL_ROWS16_GROUPS;
+        constexpr int GR = kRows16Groups;
         const int tiles = static_cast<int>((s.t_max + 64 * GR - 1) / (64 * GR));
         dim3 grid(bgs * tiles), block(256);
         if (s.d == 128) hipLaunchKernelGGL((scan_rows16_kernel<128, GR>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride);
@@ -367,10 +358,10 @@ hipError_t launch_scan(const SelShape& s, const void* qsel, const float* rq, con
             const int64_t slots = 2 * int64_t(device_cus());
             auto est = [&](int b) {
                 const int64_t wgs = int64_t(bgs) * ((s.t_max + 128 * b - 1) / (128 * b)) * s.nsplit;
-                return double((wgs + slots - 1) / slots) * b * (b == 4 ? KVSEL_SCAN_W4 : b == 3 ? 0.85 : 1.0);
+                return double((wgs + slots - 1) / slots) * b * (b == 4 ? kScanW4 : b == 3 ? 0.85 : 1.0);
             };
-            nb = kScanNB == 3 && est(3) <= est(2) ? 3 : 2;
-            if (KVSEL_SCAN_NB4 && est(4) < est(nb)) nb = 4;
+            nb = est(3) <= est(2) ? 3 : 2;
+            if (est(4) < est(nb)) nb = 4;
         }
         const int tiles = static_cast<int>((s.t_max + 4 * nb * 32 - 1) / (4 * nb * 32));
         dim3 grid(bgs * tiles * s.nsplit), block(256);

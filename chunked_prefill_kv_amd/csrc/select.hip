@@ -170,10 +170,7 @@ __global__ __launch_bounds__(256) void qcos_kernel(const T* __restrict__ q, int 
 
 // ----------------------------------------------------------------------------- exact top-k
 
-#ifndef KVSEL_TOPK_THREADS
-#define KVSEL_TOPK_THREADS 512
-#endif
-constexpr int kTopkThreads = KVSEL_TOPK_THREADS;
+constexpr int kTopkThreads = 512;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kHistBins = 2048;   // 11-bit digits
 
@@ -200,10 +197,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
     return off + incl - v;
 }
 
-#ifndef KVSEL_TOPK_LDS_KEYS
-#define KVSEL_TOPK_LDS_KEYS 30720
-#endif
-constexpr int kLdsKeys = KVSEL_TOPK_LDS_KEYS;   // problems up to this size keep their keys in LDS
+constexpr int kLdsKeys = 30720;   // problems up to this size keep their keys in LDS
 
 template <bool kLds>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores, int64_t score_stride,

@@ -20,7 +20,8 @@ namespace kvsel {
 namespace {
 
 constexpr int kBins = 4096;
-constexpr int kSeg = 2048;        // keys per segment (one workgroup of 256 threads, 8 keys each)
+constexpr int kSeg = kTopbSegKeys;   // keys per segment (one workgroup of 256 threads, 8 keys each)
+static_assert(kSeg == 8 * 256, "a segment is 8 keys per thread of a 256-thread workgroup");
 constexpr int kCap = 8192;        // boundary-bin keys kept in LDS by topb_thresh
 
 __device__ __forceinline__ int value_bin(float v) {
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
     __shared__ uint32_t hs[kBins];
     __shared__ uint32_t ck[kCap];
     __shared__ int cj[kCap];
-    __shared__ uint32_t sgt[1024], seq_[1024];      // per-segment counts (nseg <= 1024)
+    __shared__ uint32_t sgt[kTopbMaxSegments], seq_[kTopbMaxSegments];   // per-segment counts
     __shared__ uint32_t wsum[16];
     __shared__ uint32_t s_bin, s_need, s_cnt, s_digit, s_rem;
     const float* c = a.comb + static_cast<int64_t>(p) * a.s_stride;
@@ -356,7 +357,7 @@ hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int n
     a.thr = scratch + size_t(problems) * kBins;
     a.segc = a.thr + size_t(problems) * 2;
     a.out = out;
-    if (a.nseg > 1024) return hipErrorInvalidValue;    // per-segment counters live in LDS
+    if (a.nseg > kTopbMaxSegments) return hipErrorInvalidValue;   // rejected on the host before any launch
     const dim3 grid_seg(problems * a.nseg);
     if (any_select) {
         hipLaunchKernelGGL(topb_hist_kernel, grid_seg, dim3(256), 0, st, a);

@@ -108,17 +108,35 @@ typedef struct {
     const int64_t *prior_len_dev;    /* [batch] the same values in device memory */
 } kvsel_batch;
 
+/* Limits shared by kvsel_workspace_size, kvsel_select and kvsel_prefill_chunk:
+ * max_b T_b and budget are at most KVSEL_MAX_SELECT_KEYS (the exact top-B
+ * keeps one counter pair per 2048-key segment on chip); larger requests
+ * return KVSEL_ERR_UNSUPPORTED with nothing enqueued. */
+#define KVSEL_MAX_SELECT_KEYS (2048 * 1024)
+
 /* Workspace bytes that kvsel_select and kvsel_prefill_chunk need for these
- * shapes (the larger of the two).  Writes *bytes; returns a status. */
+ * shapes (the larger of the two).  Writes *bytes; returns a status (so that
+ * an invalid or unsupported shape is reported, not sized). */
 kvsel_status kvsel_workspace_size(const kvsel_heads *heads, const kvsel_batch *batch,
                                   const kvsel_params *params, size_t *bytes);
 
-/* Workspace bytes that kvsel_sparse_attn needs. */
+/* Workspace bytes that kvsel_sparse_attn needs (it lays the caller's
+ * compacted set and the chunk's keys out for the MFMA kernel and may split
+ * long key lists over several workgroups, whose partial results live here). */
 kvsel_status kvsel_sparse_attn_workspace_size(const kvsel_heads *heads, const kvsel_batch *batch,
                                               int32_t n_sel_max, size_t *bytes);
 
 /* Steps 1-3 (and the compaction of step 4 when k_sel/v_sel are given) for one
  * chunk of every sequence, against the prior cache rows [0, T_b).
+ * QuoKA article, Fig. 1(b): queries filtered by cosine dissimilarity to the
+ * mean query, then keys by query-key cosine similarity; the method paragraph
+ * after Fig. 1: max pooling over the kept queries, mean pooling over the query
+ * heads of a KV head (GQA); Fig. 1(a): the cache of each chunk is
+ * sub-selected before attention.  The pages give no formula; the steps above
+ * are the plain reading of those passages.
+ * Errors: every argument and size check returns before anything is enqueued
+ * (KVSEL_ERR_INVALID_ARG, _UNSUPPORTED, _WORKSPACE); a failed launch returns
+ * KVSEL_ERR_HIP and may leave earlier launches of the call enqueued.
  *   q       [batch][h_q][chunk_len][d]
  *   cache   read only
  *   idx     out [batch][h_kv][budget] int32: kept prior positions, ascending,
@@ -139,6 +157,13 @@ kvsel_status kvsel_select(const kvsel_heads *heads, const kvsel_batch *batch,
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /* Step 5 alone, on a compacted set supplied by the caller.
+ * QuoKA article, Fig. 1(a): the compacted cache is fed to a dense attention
+ * kernel; every chunk query attends to all compacted prior keys and, under
+ * the causal mask, to the chunk's own keys, with softmax scale 1/sqrt(d).
+ * QUILT page, "In parole semplici": the queries sharing one selected set
+ * load its entries once (here: all G query heads of a KV head and all chunk
+ * tokens read each staged key tile once per workgroup).  Multi-query
+ * attention page, "Teknisk innsikt": query head h uses KV head h / G.
  *   q                [batch][h_q][chunk_len][d]
  *   k_sel, v_sel     [batch][h_kv][n_sel_max][d]: compacted prior keys, all visible
  *   n_sel            [batch] int32 (device): rows of k_sel used per sequence, 0..n_sel_max
@@ -155,6 +180,12 @@ kvsel_status kvsel_sparse_attn(const kvsel_heads *heads, const kvsel_batch *batc
 /* One chunk of chunked prefill for every sequence: steps 1-5, then append the
  * chunk's K/V to the cache at positions [T_b, T_b + chunk_len) (the cache
  * grows by one chunk; the caller advances T_b).
+ * QuoKA article, introduction and Fig. 1(a): a long prompt is processed one
+ * chunk after another, each chunk's cache sub-selected (kvsel_select) and
+ * the compacted cache fed to dense attention (kvsel_sparse_attn); the cache
+ * grows by one chunk per step.  When T_b <= budget every prior key is kept
+ * and steps 1-3 are skipped for that sequence.
+ * Errors: as kvsel_select.
  *   q, k_chunk, v_chunk, out  as in kvsel_sparse_attn
  *   cache   prior rows are read, rows [T_b, T_b + chunk_len) are written;
  *           capacity (contiguous) or the block table (paged) must cover them
@@ -165,6 +196,26 @@ kvsel_status kvsel_prefill_chunk(const kvsel_heads *heads, const kvsel_batch *ba
                                  const kvsel_cache *cache, void *out, int32_t out_dtype,
                                  int32_t *idx, void *workspace, size_t workspace_bytes,
                                  void *stream);
+
+/* Where kvsel_prefill_chunk leaves the compacted key list of step 4 in the
+ * workspace, so that a caller can read it back after the call (QuoKA article,
+ * Fig. 1(a): the compacted cache handed to attention).  For the shapes and
+ * cache given (only its layout is read):
+ *   *packed = 1 when the call builds the lists in the workspace, 0 when its
+ *     attention reads the kept rows in place (no lists; the other outputs are
+ *     then left unwritten);
+ *   keys at byte offset *k_offset: [batch][h_kv][*slots][d] (one row per slot);
+ *   values at *v_offset: [batch][h_kv][d][*slots] (transposed) when
+ *     *v_transposed, else [batch][h_kv][*slots][d];
+ *   slot s of sequence b holds, for s < n_b = min(budget, T_b), the prior row
+ *   at idx[b][g][s]; for n_b <= s < n_b + chunk_len, the chunk's row s - n_b;
+ *   beyond, zeros.
+ * The lists are valid until the next call that uses the workspace.  Returns a
+ * status; pure host arithmetic (nothing is enqueued). */
+kvsel_status kvsel_compacted_view(const kvsel_heads *heads, const kvsel_batch *batch,
+                                  const kvsel_params *params, const kvsel_cache *cache,
+                                  int32_t *packed, size_t *k_offset, size_t *v_offset,
+                                  int32_t *slots, int32_t *v_transposed);
 
 /* Per-kernel timing (a tracing aid for benchmarks).  After
  * kvsel_trace_start(mask), every launch of a kernel whose bit (1 << id) is

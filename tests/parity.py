@@ -9,7 +9,8 @@ Rules (tolerances written here, derived in the design notes):
          (the integer decision taken in the kernel's precision), and
          (b) it equals the oracle's set except positions whose oracle score
          lies within IDX_BAND of the B-th score; sets have equal size;
-  gather bit-exact;
+  gather bit-exact, both the kvsel_select gather and the compacted lists
+         kvsel_prefill_chunk hands to its attention;
   O      max |O_gpu - O_oracle| <= 1e-4 (fp32 inputs) or 2e-2 (bf16 inputs),
          given the same index set.
 """
@@ -66,3 +67,36 @@ def check_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str) -> floa
     err = float(np.abs(got - ref).max()) if got.size else 0.0
     assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
     return err
+
+
+def check_compaction(h, b, p, cache, ws, Ts, C, idx, prior_kv, chunk_kv, heads=None):
+    """Rule 3 on the timed path: after kvsel_prefill_chunk, the compacted key
+    list (and the value list, transposed for bf16) left in the workspace holds,
+    bit for bit, the prior rows at idx, then the chunk's rows, then zeros.
+    prior_kv[s] / chunk_kv[s]: (K, V) bit arrays [H_kv][rows][d] of sequence s.
+    Returns False when the call builds no lists (gathering attention)."""
+    from chunked_prefill_kv_amd import kvsel as K
+    v = K.compacted_view(h, b, p, cache)
+    if v is None:
+        return False
+    nb, H_kv, d, slots = len(Ts), h.h_kv, h.d, v["slots"]
+    store = np.uint16 if h.dtype == K.KVSEL_BF16 else np.uint32
+    esz = np.dtype(store).itemsize
+    n_el = nb * H_kv * slots * d
+    raw = ws.cpu().numpy()
+    kl = raw[v["k_offset"]:v["k_offset"] + n_el * esz].view(store).reshape(nb, H_kv, slots, d)
+    vl = raw[v["v_offset"]:v["v_offset"] + n_el * esz].view(store)
+    vl = vl.reshape(nb, H_kv, d, slots).transpose(0, 1, 3, 2) if v["v_transposed"] else vl.reshape(nb, H_kv, slots, d)
+    B = p.budget
+    for s, T in enumerate(Ts):
+        n = min(B, T)
+        for g in (range(H_kv) if heads is None else heads):
+            for lst, pk, ck, what in ((kl, prior_kv[s][0], chunk_kv[s][0], "K"), (vl, prior_kv[s][1], chunk_kv[s][1], "V")):
+                want = np.zeros((slots, d), dtype=store)
+                if n:
+                    want[:n] = pk[g, idx[s, g, :n]].view(store)
+                want[n:n + C] = ck[g].view(store)
+                got = lst[s, g]
+                bad = np.nonzero(np.any(got != want, axis=1))[0]
+                assert bad.size == 0, f"compacted {what} seq {s} head {g}: {bad.size} slots differ, first {bad[:5]} (n={n}, C={C})"
+    return True

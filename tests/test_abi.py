@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(K.LIB_PATH)
     for name in _declared():
         assert hasattr(lib, name), name
-    assert K.version() == 101
+    assert K.version() == 102
 
 
 def _bad(h=None, b=None, p=None):
@@ -97,3 +97,48 @@ def test_calls_reject_before_enqueue():
     st = lib.kvsel_sparse_attn(ctypes.byref(h), ctypes.byref(b), fake, fake, fake, fake, 16, fake, fake, fake, 9,
                                fake, 1 << 30, None)
     assert st == K.KVSEL_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("T,B", [(1 << 21, 4096), ((1 << 21) + 1, 4096), (2048, (1 << 21) + 1), (100, 1 << 22)])
+def test_selection_limit_rejected_on_host(T, B):
+    """Prior lengths or budgets above 2^21 keys cannot be selected from (the
+    top-B's per-segment counters live on chip): every sizing or launching
+    entry point refuses them with UNSUPPORTED before anything is enqueued;
+    2^21 itself is accepted."""
+    h, p = K.heads(32, 8, 128, K.KVSEL_BF16), K.Params(256, B)
+    b = K.batch([T], 2048, None)
+    st, _ = _status(h, b, p)
+    ok = max(T, B) <= (1 << 21)
+    assert st == (K.KVSEL_OK if ok else K.KVSEL_ERR_UNSUPPORTED), K.last_error()
+    if ok:
+        return
+    assert "2097152" in K.last_error()
+    lib, fake = K.load(), 1 << 20
+    c = K.Cache(fake, fake, T + 4096, 0, 0, None)
+    for call in ("select", "prefill"):
+        if call == "select":
+            st = lib.kvsel_select(ctypes.byref(h), ctypes.byref(b), ctypes.byref(p), fake, ctypes.byref(c), fake,
+                                  None, None, None, None, fake, 1 << 40, None)
+        else:
+            st = lib.kvsel_prefill_chunk(ctypes.byref(h), ctypes.byref(b), ctypes.byref(p), fake, fake, fake,
+                                         ctypes.byref(c), fake, K.KVSEL_BF16, None, fake, 1 << 40, None)
+        assert st == K.KVSEL_ERR_UNSUPPORTED, (call, K.last_error())
+
+
+def test_compacted_view_host_arithmetic():
+    """The compacted lists sit inside the workspace, after the selection's
+    buffers; the gathering attention (one 128-row block per KV head) builds
+    none."""
+    h, p = K.heads(32, 8, 128, K.KVSEL_BF16), K.Params(256, 4096)
+    b = K.batch([30720], 2048, None)
+    b.prior_len_dev = 256
+    fake = 1 << 20
+    c = K.Cache(fake, fake, 32768, 0, 0, None)
+    v = K.compacted_view(h, b, p, c)
+    st, ws = _status(h, K.batch([30720], 2048, None), p)
+    assert v is not None and v["v_transposed"] and v["slots"] == 4096 + 2048
+    assert v["k_offset"] % 256 == 0 and v["v_offset"] >= v["k_offset"] + 8 * v["slots"] * 128 * 2
+    assert v["v_offset"] + 8 * v["slots"] * 128 * 2 <= ws
+    b1 = K.batch([4096] * 4, 1, None)
+    b1.prior_len_dev = 256
+    assert K.compacted_view(h, b1, K.Params(1, 2048), K.Cache(fake, fake, 8192, 0, 0, None)) is None

@@ -41,6 +41,10 @@ def _sampled_chunk(r, chunks, k, heads, pooling="head"):
     assert np.array_equal(r.idx[k][0].cpu().numpy(), idx_h)
     Og = r.outs[k][0].float().cpu().numpy().astype(np.float64)
     ks_h, vs_h = runner.to_host_bits(ks[0]), runner.to_host_bits(vs[0])
+    # the compacted lists the timed attention consumed, bit for bit, on every KV head
+    pk = (np.concatenate([c[1] for c in chunks[:k]], axis=1), np.concatenate([c[2] for c in chunks[:k]], axis=1)) \
+        if k else (None, None)
+    parity.check_compaction(r.h, r.batches[k], r.p, r.cache, r.ws, [T], C, idx_h[None], [pk], [(chunks[k][1], chunks[k][2])])
     recall = []
     for g in heads:
         hs = slice(g * G, (g + 1) * G)
@@ -48,7 +52,9 @@ def _sampled_chunk(r, chunks, k, heads, pooling="head"):
         kp_bits = np.concatenate([c[1][g:g + 1] for c in chunks[:k]], axis=1)
         vp_bits = np.concatenate([c[2][g:g + 1] for c in chunks[:k]], axis=1)
         Kp, Vp = gen.to_f64(kp_bits), gen.to_f64(vp_bits)
-        if group:
+        if T <= wl.B:                          # nothing to select: every prior key kept
+            assert np.array_equal(idx_h[g, :T], np.arange(T)) and np.all(idx_h[g, T:] == -1)
+        elif group:
             Qbar = quoka.pooled_queries(Qc, 1)
             parity.check_keep(Qbar[0], wl.n_q, keep_h[g])
             S_or = quoka.key_scores_group(Qbar, [np.sort(keep_h[g])], Kp)[0]
@@ -56,8 +62,9 @@ def _sampled_chunk(r, chunks, k, heads, pooling="head"):
             for i, h in enumerate(range(g * G, (g + 1) * G)):
                 parity.check_keep(Qc[i], wl.n_q, keep_h[h])
             S_or = quoka.key_scores(Qc, [np.sort(keep_h[h]) for h in range(g * G, (g + 1) * G)], Kp)[0]
-        parity.check_close(S_h[g, :T], S_or, parity.S_TOL, f"S chunk {k} head {g}")
-        parity.check_idx(S_or, wl.B, idx_h[g], S_h[g, :T])
+        if T > wl.B:
+            parity.check_close(S_h[g, :T], S_or, parity.S_TOL, f"S chunk {k} head {g}")
+            parity.check_idx(S_or, wl.B, idx_h[g], S_h[g, :T])
         n = min(wl.B, T)
         sel = idx_h[g, :n]
         assert np.array_equal(ks_h[g, :n], kp_bits[0, sel]) and np.array_equal(vs_h[g, :n], vp_bits[0, sel])
@@ -68,9 +75,12 @@ def _sampled_chunk(r, chunks, k, heads, pooling="head"):
     return recall
 
 
+ALL8 = list(range(8))
+
+
 @pytest.mark.parametrize("name,sample", [
-    ("llama8b_32k", {8: [0, 5], 15: [3, 7]}),      # the bench workload: a mid and the last chunk
-    ("mqa_64k", {31: [0]}),                        # the single shared KV head, last chunk
+    ("llama8b_32k", {2: ALL8, 8: ALL8, 15: ALL8}),  # the bench workload: T = B, a mid and the last chunk, every KV head
+    ("mqa_64k", {5: [0], 31: [0]}),                 # the single shared KV head: first selecting and last chunk
     ("tiny_f32", {3: [0, 1], 7: [0, 1]}),
 ])
 def test_fullsize_prefill_sampled(name, sample):
@@ -93,7 +103,7 @@ def test_fullsize_prefill_group_pooling_sampled():
     chunks = [gen.chunk_inputs(wl, k) for k in range(wl.n_chunks)]
     r = runner.PromptRunner(wl, out_dtype=torch.bfloat16, pooling=K.KVSEL_POOL_GROUP)
     r.load(chunks, keep_idx=True)
-    sample = {9: [2], 15: [6]}
+    sample = {9: ALL8, 15: ALL8}
     for k in range(wl.n_chunks):
         if k in sample:
             _sampled_chunk(r, chunks, k, sample[k], pooling="group")
@@ -102,8 +112,8 @@ def test_fullsize_prefill_group_pooling_sampled():
 
 
 def test_fullsize_gqa_128k_last_chunk_and_needles():
-    """The 128K GQA layer: the last chunk on KV head 0, and the recall of the
-    64 planted needles at their chunks (a diagnostic of the selection)."""
+    """The 128K GQA layer: the last chunk on every KV head, and the recall of
+    the 64 planted needles at their chunks (a diagnostic of the selection)."""
     wl = gen.WORKLOADS["gqa_128k"]
     print("[case] full-size prefill gqa_128k", flush=True)
     chunks = [gen.chunk_inputs(wl, k) for k in range(wl.n_chunks)]
@@ -111,15 +121,15 @@ def test_fullsize_gqa_128k_last_chunk_and_needles():
     r.load(chunks, keep_idx=True)
     for k in range(wl.n_chunks - 1):
         r.run_chunk(k)
-    _sampled_chunk(r, chunks, wl.n_chunks - 1, [0])
+    _sampled_chunk(r, chunks, wl.n_chunks - 1, ALL8)
     hits = sum(int(nd.pos in set(r.idx[nd.chunk][0, nd.head // wl.G].cpu().numpy().tolist()))
                for nd in gen.needles(wl))
     print(f"needle recall {hits}/{wl.needles}")
     assert hits >= wl.needles // 2
 
 
-def test_fullsize_decode_sampled():
-    """64 ragged sequences (4K-64K) over a paged cache; 4 sequences checked."""
+def test_fullsize_decode_all_sequences():
+    """64 ragged sequences (4K-64K) over a paged cache, every sequence checked."""
     wl = gen.WORKLOADS["decode_paged"]
     print("[case] full-size decode", flush=True)
     di = gen.decode_inputs(wl)
@@ -132,7 +142,7 @@ def test_fullsize_decode_sampled():
     torch.cuda.synchronize()
     assert np.array_equal(idx.cpu().numpy(), dr.idx.cpu().numpy())
     O = dr.out.float().cpu().numpy().astype(np.float64)
-    for b in [0, 17, 40, 63]:
+    for b in range(wl.batch):
         T = int(di.prior_len[b])
         kp, vp = di.logical_kv(b, wl.block_size)
         Kp, Vp = gen.to_f64(kp), gen.to_f64(vp)

@@ -74,6 +74,11 @@ def check_chunk(r: runner.PromptRunner, k: int, chunks, c64, heads=None, pooling
     torch.cuda.synchronize()
     idx_h = idx[0].cpu().numpy()
     assert np.array_equal(r.idx[k][0].cpu().numpy(), idx_h), "prefill_chunk and select disagree on idx"
+    # the compacted lists the attention consumed, bit for bit (rule 3 on the prefill path)
+    pk = (np.concatenate([c[1] for c in chunks[:k]], axis=1), np.concatenate([c[2] for c in chunks[:k]], axis=1)) \
+        if k else (None, None)
+    parity.check_compaction(r.h, r.batches[k], r.p, r.cache, r.ws, [T], C, idx_h[None], [pk], [(chunks[k][1], chunks[k][2])],
+                     heads)
     G = wl.G
     heads = range(wl.H_kv) if heads is None else heads
     qh = [h for g in heads for h in range(g * G, (g + 1) * G)]
@@ -356,6 +361,8 @@ def test_batched_prefill_ragged(C, Ts, B):
     K.kvsel_prefill_chunk(h, b, p, q, kn, vn, cache, out, idx2, ws)
     torch.cuda.synchronize()
     assert np.array_equal(idx.cpu().numpy(), idx2.cpu().numpy())
+    parity.check_compaction(h, b, p, cache, ws, Ts, C, idx2.cpu().numpy(), [(kc[s, :, :T], vc[s, :, :T]) for s, T in enumerate(Ts)],
+                     [(c[1], c[2]) for c in cur])
     kc_after, vc_after = runner.to_host_bits(kc_d), runner.to_host_bits(vc_d)
     O = out.double().cpu().numpy()
     G = wl.G
@@ -438,6 +445,7 @@ def test_batched_prefill_paged(C, Ts, B, bs):
     K.kvsel_prefill_chunk(h, b, p, q, kn, vn, cache, out, idx2, ws)
     torch.cuda.synchronize()
     assert np.array_equal(idx.cpu().numpy(), idx2.cpu().numpy())
+    parity.check_compaction(h, b, p, cache, ws, Ts, C, idx2.cpu().numpy(), logical, [(c[1], c[2]) for c in cur])
     kpa, vpa = runner.to_host_bits(kp_d), runner.to_host_bits(vp_d)
     O = out.double().cpu().numpy()
     for s, T in enumerate(Ts):
@@ -465,3 +473,98 @@ def test_batched_prefill_paged(C, Ts, B, bs):
         O_or = quoka.attend(Qc, [Kp[g, idx_h[g, :n]] for g in range(wl.H_kv)],
                             [Vp[g, idx_h[g, :n]] for g in range(wl.H_kv)], Kn, Vn)
         parity.check_close(O[s], O_or, parity.o_tol(wl.dtype), f"O seq {s}")
+
+
+def test_sparse_attn_empty_set_without_arrays():
+    """n_sel_max = 0 with no compacted arrays at all (k_sel = v_sel = NULL, as
+    the header allows): every query attends to the chunk's own keys only,
+    causally; checked against the oracle with empty selected sets."""
+    wl = LLAMA.replace(L=1400, C=700, H_q=8, H_kv=2, n_q=100, B=900)
+    print("[case] sparse_attn n_sel_max=0, NULL k_sel/v_sel", flush=True)
+    chunks = [gen.chunk_inputs(wl, k, seq=s) for s, k in enumerate([0, 1])]
+    dev = "cuda"
+    q = runner.to_device(np.stack([c[0] for c in chunks]), dev)
+    kc = runner.to_device(np.stack([c[1] for c in chunks]), dev)
+    vc = runner.to_device(np.stack([c[2] for c in chunks]), dev)
+    h = K.heads(wl.H_q, wl.H_kv, wl.d, K.KVSEL_BF16)
+    bt = K.batch([0, 0], wl.C, None)
+    nsel = torch.zeros(2, dtype=torch.int32, device=dev)
+    ws = torch.empty(K.sparse_attn_workspace_size(h, bt, 0), dtype=torch.uint8, device=dev)
+    out = torch.empty(2, wl.H_q, wl.C, wl.d, dtype=torch.float32, device=dev)
+    K.kvsel_sparse_attn(h, bt, q, None, None, nsel, 0, kc, vc, out, ws)
+    torch.cuda.synchronize()
+    O = out.double().cpu().numpy()
+    empty = np.zeros((0, wl.d))
+    for s, c in enumerate(chunks):
+        Qc, Kc, Vc = (gen.to_f64(x) for x in c)
+        ref = quoka.attend(Qc, [empty] * wl.H_kv, [empty] * wl.H_kv, Kc, Vc)
+        parity.check_close(O[s], ref, parity.o_tol("bf16"), f"O seq {s}")
+
+
+@pytest.mark.parametrize("dup", [12000, 9000])
+def test_topb_boundary_bin_over_capacity(dup):
+    """More than 8192 prior keys share the value bin of the B-th score (an
+    exact-duplicate key row repeated `dup` times, plus near-duplicates one
+    bf16 step apart in a few coordinates): the top-B's threshold search then
+    works over the whole score row instead of the on-chip boundary list.  The
+    kept set must be the exact top-B of the GPU's own scores (ties to the lower
+    index) and match the oracle outside the 1e-4 band."""
+    rng = np.random.default_rng([0x5EED, 4242, dup])
+    H_q, H_kv, d, C, T = 4, 1, 128, 64, 20480
+    base = gen.WORKLOADS["llama8b_32k"]
+    wl = base.replace(L=T + C, C=C, H_q=H_q, H_kv=H_kv, n_q=8, B=1)
+    q = gen.f32_to_bf16_bits((0.5 * rng.standard_normal((H_q, C, d)) + 1.0).astype(np.float32))
+    other = (0.5 * rng.standard_normal((T, d)) + 0.3 * rng.standard_normal(d)).astype(np.float32)
+    row = (0.5 * rng.standard_normal(d) + 1.0).astype(np.float32)
+    keys = gen.f32_to_bf16_bits(other)
+    pos = rng.permutation(T)
+    dup_pos, near_pos = pos[:dup], pos[dup:dup + 2000]
+    rb = gen.f32_to_bf16_bits(row[None])[0]
+    keys[dup_pos] = rb
+    near = np.repeat(rb[None], len(near_pos), axis=0).astype(np.int32)
+    big = np.nonzero(np.abs(row) > 0.25)[0]                # coordinates far from zero: +-1 on the bits is +-1 ulp
+    cols = big[rng.integers(0, len(big), size=(len(near_pos), 3))]
+    steps = rng.choice([-1, 1], size=(len(near_pos), 3))
+    for j in range(3):
+        near[np.arange(len(near_pos)), cols[:, j]] += steps[:, j]           # one bf16 ulp per coordinate
+    keys[near_pos] = near.astype(np.uint16)
+    Q64, K64 = gen.to_f64(q), gen.to_f64(keys)[None]
+    keep = [quoka.query_keep(Q64[hh], wl.n_q) for hh in range(H_q)]
+    S_or = quoka.key_scores(Q64, keep, K64)[0]
+    s_dup = S_or[dup_pos[0]]
+    above = int(np.sum(S_or > s_dup + 1e-9))
+    B = above + dup // 2                      # the B-th score falls among the duplicates
+    print(f"[case] top-B boundary bin: {dup} duplicates, {above} keys above them, B={B}", flush=True)
+    dev = "cuda"
+    kcache = np.zeros((1, H_kv, T, d), dtype=np.uint16)
+    kcache[0, 0] = keys
+    vcache = gen.f32_to_bf16_bits(rng.standard_normal((1, H_kv, T, d)).astype(np.float32))
+    h = K.heads(H_q, H_kv, d, K.KVSEL_BF16)
+    p = K.Params(wl.n_q, B)
+    prior = torch.tensor([T], dtype=torch.int64, device=dev)
+    b = K.batch([T], C, prior)
+    kd, vd = runner.to_device(kcache, dev), runner.to_device(vcache, dev)
+    cache = K.cache(kd, vd, T)
+    ws = torch.empty(K.workspace_size(h, b, p), dtype=torch.uint8, device=dev)
+    idx = torch.full((1, H_kv, B), -7, dtype=torch.int32, device=dev)
+    keep_d = torch.full((1, H_q, wl.n_q), -7, dtype=torch.int32, device=dev)
+    S = torch.full((1, H_kv, T), float("nan"), dtype=torch.float32, device=dev)
+    ks = torch.empty(1, H_kv, B, d, dtype=torch.bfloat16, device=dev)
+    vs = torch.empty_like(ks)
+    K.kvsel_select(h, b, p, runner.to_device(q[None], dev), cache, idx, ks, vs, keep_d, S, ws)
+    torch.cuda.synchronize()
+    keep_h = keep_d[0].cpu().numpy()
+    for hh in range(H_q):
+        parity.check_keep(Q64[hh], wl.n_q, keep_h[hh])
+    S_c = quoka.key_scores(Q64, [np.sort(keep_h[hh]) for hh in range(H_q)], K64)[0]
+    S_h, idx_h = S[0, 0].cpu().numpy(), idx[0, 0].cpu().numpy()
+    parity.check_close(S_h, S_c, parity.S_TOL, "S")
+    # the GPU's boundary bin really holds more than 8192 keys
+    thr = np.sort(S_h)[::-1][B - 1]
+    in_bin = np.sum(np.floor((S_h.astype(np.float32) + np.float32(1)) * np.float32(2048)) ==
+                    np.floor((np.float32(thr) + np.float32(1)) * np.float32(2048)))
+    assert in_bin > 8192, in_bin
+    parity.check_idx(S_c, B, idx_h, S_h)
+    n = B
+    assert np.array_equal(runner.to_host_bits(ks[0, 0])[:n], keys[idx_h[:n]])
+    assert np.array_equal(runner.to_host_bits(vs[0, 0])[:n], vcache[0, 0, idx_h[:n]])
