@@ -258,8 +258,10 @@ Layout layout(const SelShape& s, bool with_attn) {
     const int64_t nsel_max = s.budget < s.t_max ? s.budget : s.t_max;
     L.nk_pad = static_cast<int>(round_up(nsel_max + s.C, 64));
     if (with_attn) {
-        L.kall = take(bg * L.nk_pad * s.d * s.esz);
-        L.vall = take(bg * L.nk_pad * s.d * s.esz);
+        if (!attn_use_gather(s)) {           // the gathering attention reads the kept rows in place
+            L.kall = take(bg * L.nk_pad * s.d * s.esz);
+            L.vall = take(bg * L.nk_pad * s.d * s.esz);
+        }
         L.apart = take(attn_part_bytes(s));
     }
     L.total = off;
@@ -268,8 +270,15 @@ Layout layout(const SelShape& s, bool with_attn) {
 
 // Whether kvsel_prefill_chunk takes the gathering attention (kept rows read in
 // place through their cache row numbers, no packed lists) for these shapes.
-bool prefill_uses_gather(const SelShape& s, const kvsel_cache* c, const kvsel_heads* h, const kvsel_batch* b) {
-    return attn_use_gather(s) && cache_rows_fit(c, h, b);
+// (A gathering shape whose cache holds 2^31 rows or more is refused, see
+// check_gather_rows: its workspace has no room for packed lists.)
+bool prefill_uses_gather(const SelShape& s) { return attn_use_gather(s); }
+
+kvsel_status check_gather_rows(const SelShape& s, const kvsel_cache* c, const kvsel_heads* h, const kvsel_batch* b) {
+    if (attn_use_gather(s) && !cache_rows_fit(c, h, b))
+        return fail(KVSEL_ERR_UNSUPPORTED, "chunks of %d tokens x %d query heads per KV head read the cache through "
+                    "int32 row numbers: a cache of 2^31 rows or more is not supported", s.C, s.G);
+    return KVSEL_OK;
 }
 
 template <typename P> P* at(void* ws, size_t off) { return reinterpret_cast<P*>(static_cast<char*>(ws) + off); }
@@ -323,6 +332,58 @@ kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, 
     KVSEL_TRY(traced(KVSEL_K_TOPB, st, [&] { return launch_topb(s.batch * s.h_kv, s.h_kv, S, sc.nsplit, split_stride, comb, s.t_max, T,
                                                                 s.budget, s.t_max, any, at<uint32_t>(ws, L.topb), idx, st,
                                                                 rowidx ? &cv : nullptr, rowidx); }), "key top-B");
+    return KVSEL_OK;
+}
+
+// Checks of kvsel_prefill_chunk.
+kvsel_status check_prefill(const kvsel_heads* heads, const kvsel_batch* batch, const kvsel_params* params,
+                           const void* q, const void* k_chunk, const void* v_chunk, const kvsel_cache* cache,
+                           int32_t out_dtype, const void* out, int64_t* t_max) {
+    kvsel_status st;
+    if ((st = check_heads(heads)) || (st = check_batch(batch, true, t_max)) || (st = check_params(params)) ||
+        (st = check_select(*t_max, params)) || (st = check_cache(cache, batch, batch->chunk_len)))
+        return st;
+    if (!q || !k_chunk || !v_chunk || !out) return fail(KVSEL_ERR_INVALID_ARG, "q/k_chunk/v_chunk/out is NULL");
+    if (!aligned16(q) || !aligned16(k_chunk) || !aligned16(v_chunk) || !aligned16(out))
+        return fail(KVSEL_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    if (out_dtype != KVSEL_F32 && out_dtype != KVSEL_BF16) return fail(KVSEL_ERR_INVALID_ARG, "out_dtype=%d unknown", out_dtype);
+    return KVSEL_OK;
+}
+
+// One chunk of every sequence on a checked workspace: steps 1-5 and the append.
+kvsel_status run_prefill(const kvsel_heads* heads, const kvsel_batch* batch, const SelShape& s, const Layout& L,
+                         const void* q, const void* k_chunk, const void* v_chunk, const kvsel_cache* cache,
+                         void* out, int32_t out_dtype, int32_t* idx, void* workspace, hipStream_t hs) {
+    kvsel_status st;
+    const CacheView cv = make_view(cache, heads);
+    int32_t* idx_buf = idx ? idx : at<int32_t>(workspace, L.idx);
+    const bool gather = prefill_uses_gather(s);
+    int32_t* rowidx = gather ? at<int32_t>(workspace, L.rowidx) : nullptr;
+    if ((st = run_select(s, batch, q, cv, workspace, L, idx_buf, nullptr, nullptr, hs, rowidx))) return st;
+    PackSrc src{};
+    src.cache = &cv;
+    src.prior_len = batch->prior_len_dev;
+    src.budget = s.budget;
+    src.idx = idx_buf;
+    src.idx_stride = s.budget;
+    src.append = true;
+    int32_t* nsel = at<int32_t>(workspace, L.nsel);
+    const float scale = heads->scale > 0.0f ? heads->scale : 1.0f / std::sqrt(static_cast<float>(heads->d));
+    if (gather) {
+        // fused gather: the attention reads the kept rows from the cache itself
+        // (row numbers from the top-B); the append runs on its own (it writes
+        // rows [T_b, T_b + C), which neither the selection nor the attention reads)
+        AttnGather ga{cv, batch->prior_len_dev, s.budget, rowidx, s.budget, k_chunk, v_chunk};
+        KVSEL_TRY(traced(KVSEL_K_ATTN, hs, [&] { return launch_attn(s, q, nullptr, nullptr, nullptr, 0, scale, out, out_dtype == KVSEL_F32,
+                              at<float>(workspace, L.apart), hs, &ga); }), "attention");
+        KVSEL_TRY(traced(KVSEL_K_APPEND, hs, [&] { return launch_append(s, cv, batch->prior_len_dev, k_chunk, v_chunk, hs); }), "cache append");
+        return KVSEL_OK;
+    }
+    KVSEL_TRY(traced(KVSEL_K_PACK, hs, [&] { return launch_pack(s, src, k_chunk, v_chunk, L.nk_pad, at<void>(workspace, L.kall), at<void>(workspace, L.vall),
+                          nsel, hs); }), "pack");
+    KVSEL_TRY(traced(KVSEL_K_ATTN, hs, [&] { return launch_attn(s, q, at<void>(workspace, L.kall), at<void>(workspace, L.vall), nsel, L.nk_pad, scale, out,
+                          out_dtype == KVSEL_F32, at<float>(workspace, L.apart), hs); }), "attention");
+    // here the cache append happens inside the pack kernel (it reads the chunk's rows anyway)
     return KVSEL_OK;
 }
 
@@ -395,7 +456,8 @@ kvsel_status kvsel_compacted_view(const kvsel_heads* heads, const kvsel_batch* b
         return fail(KVSEL_ERR_INVALID_ARG, "an output pointer is NULL");
     const SelShape s = make_shape(heads, batch, params, t_max);
     const Layout L = layout(s, true);
-    *packed = prefill_uses_gather(s, cache, heads, batch) ? 0 : 1;
+    if ((st = check_gather_rows(s, cache, heads, batch))) return st;
+    *packed = prefill_uses_gather(s) ? 0 : 1;
     *k_offset = L.kall;
     *v_offset = L.vall;
     *slots = L.nk_pad;
@@ -484,47 +546,13 @@ kvsel_status kvsel_prefill_chunk(const kvsel_heads* heads, const kvsel_batch* ba
     g_err.clear();
     kvsel_status st;
     int64_t t_max;
-    if ((st = check_heads(heads)) || (st = check_batch(batch, true, &t_max)) || (st = check_params(params)) ||
-        (st = check_select(t_max, params)) || (st = check_cache(cache, batch, batch->chunk_len)))
-        return st;
-    if (!q || !k_chunk || !v_chunk || !out) return fail(KVSEL_ERR_INVALID_ARG, "q/k_chunk/v_chunk/out is NULL");
-    if (!aligned16(q) || !aligned16(k_chunk) || !aligned16(v_chunk) || !aligned16(out))
-        return fail(KVSEL_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
-    if (out_dtype != KVSEL_F32 && out_dtype != KVSEL_BF16) return fail(KVSEL_ERR_INVALID_ARG, "out_dtype=%d unknown", out_dtype);
+    if ((st = check_prefill(heads, batch, params, q, k_chunk, v_chunk, cache, out_dtype, out, &t_max))) return st;
     const SelShape s = make_shape(heads, batch, params, t_max);
+    if ((st = check_gather_rows(s, cache, heads, batch))) return st;
     const Layout L = layout(s, true);
     if ((st = check_ws(workspace, workspace_bytes, L.total))) return st;
-    const CacheView cv = make_view(cache, heads);
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    int32_t* idx_buf = idx ? idx : at<int32_t>(workspace, L.idx);
-    const bool gather = prefill_uses_gather(s, cache, heads, batch);
-    int32_t* rowidx = gather ? at<int32_t>(workspace, L.rowidx) : nullptr;
-    if ((st = run_select(s, batch, q, cv, workspace, L, idx_buf, nullptr, nullptr, hs, rowidx))) return st;
-    PackSrc src{};
-    src.cache = &cv;
-    src.prior_len = batch->prior_len_dev;
-    src.budget = s.budget;
-    src.idx = idx_buf;
-    src.idx_stride = s.budget;
-    src.append = true;
-    int32_t* nsel = at<int32_t>(workspace, L.nsel);
-    const float scale = heads->scale > 0.0f ? heads->scale : 1.0f / std::sqrt(static_cast<float>(heads->d));
-    if (gather) {
-        // fused gather: the attention reads the kept rows from the cache itself
-        // (row numbers from the top-B); the append runs on its own (it writes
-        // rows [T_b, T_b + C), which neither the selection nor the attention reads)
-        AttnGather ga{cv, batch->prior_len_dev, s.budget, rowidx, s.budget, k_chunk, v_chunk};
-        KVSEL_TRY(traced(KVSEL_K_ATTN, hs, [&] { return launch_attn(s, q, nullptr, nullptr, nullptr, 0, scale, out, out_dtype == KVSEL_F32,
-                              at<float>(workspace, L.apart), hs, &ga); }), "attention");
-        KVSEL_TRY(traced(KVSEL_K_APPEND, hs, [&] { return launch_append(s, cv, batch->prior_len_dev, k_chunk, v_chunk, hs); }), "cache append");
-        return KVSEL_OK;
-    }
-    KVSEL_TRY(traced(KVSEL_K_PACK, hs, [&] { return launch_pack(s, src, k_chunk, v_chunk, L.nk_pad, at<void>(workspace, L.kall), at<void>(workspace, L.vall),
-                          nsel, hs); }), "pack");
-    KVSEL_TRY(traced(KVSEL_K_ATTN, hs, [&] { return launch_attn(s, q, at<void>(workspace, L.kall), at<void>(workspace, L.vall), nsel, L.nk_pad, scale, out,
-                          out_dtype == KVSEL_F32, at<float>(workspace, L.apart), hs); }), "attention");
-    // here the cache append happens inside the pack kernel (it reads the chunk's rows anyway)
-    return KVSEL_OK;
+    return run_prefill(heads, batch, s, L, q, k_chunk, v_chunk, cache, out, out_dtype, idx, workspace,
+                       static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
