@@ -79,11 +79,19 @@ struct Trace {
 };
 Trace g_trace;
 
+// Set while a call must not create trace events (the no-allocation entry point).
+thread_local bool g_no_trace = false;
+struct NoTraceScope {
+    bool prev;
+    NoTraceScope() : prev(g_no_trace) { g_no_trace = true; }
+    ~NoTraceScope() { g_no_trace = prev; }
+};
+
 // Launch `fn` (returning hipError_t), bracketed by events when kernel `id` is traced.
 template <typename F>
 hipError_t traced(int id, hipStream_t st, F&& fn) {
     hipEvent_t a = nullptr, b = nullptr;
-    {
+    if (!g_no_trace) {
         std::lock_guard<std::mutex> lk(g_trace.mu);
         if (g_trace.mask & (1u << id)) {
             a = g_trace.take();
@@ -335,7 +343,7 @@ kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, 
     return KVSEL_OK;
 }
 
-// Checks of kvsel_prefill_chunk.
+// Checks shared by kvsel_prefill_chunk and kvsel_prefill_chunk_noalloc.
 kvsel_status check_prefill(const kvsel_heads* heads, const kvsel_batch* batch, const kvsel_params* params,
                            const void* q, const void* k_chunk, const void* v_chunk, const kvsel_cache* cache,
                            int32_t out_dtype, const void* out, int64_t* t_max) {
@@ -384,6 +392,38 @@ kvsel_status run_prefill(const kvsel_heads* heads, const kvsel_batch* batch, con
     KVSEL_TRY(traced(KVSEL_K_ATTN, hs, [&] { return launch_attn(s, q, at<void>(workspace, L.kall), at<void>(workspace, L.vall), nsel, L.nk_pad, scale, out,
                           out_dtype == KVSEL_F32, at<float>(workspace, L.apart), hs); }), "attention");
     // here the cache append happens inside the pack kernel (it reads the chunk's rows anyway)
+    return KVSEL_OK;
+}
+
+// ----------------------------------------------------------------------------- fixed scratch (no-allocation entry)
+//
+// kvsel_prefill_chunk_noalloc takes its workspace from this array instead of
+// a caller buffer.  Each GPU the library runs on holds its own copy (from the
+// first call on that GPU until the process ends).  In host code `scratch` only
+// names the symbol: its device address, different on every GPU, comes from
+// hipGetSymbolAddress once per device (with that device current) and only
+// that address is handed to kernels.  Nothing here requires the array to
+// start zeroed: every kernel writes what a later one reads (the top-B
+// histogram is cleared by the first selection kernel of each call).
+constexpr size_t kNoAllocScratchBytes = KVSEL_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+kvsel_status scratch_address(void** out) {
+    int dev = -1;
+    KVSEL_TRY(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(KVSEL_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        KVSEL_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (!p || (reinterpret_cast<uintptr_t>(p) & 255u)) return fail(KVSEL_ERR_HIP, "scratch address %p not 256-byte aligned", p);
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
     return KVSEL_OK;
 }
 
@@ -552,6 +592,27 @@ kvsel_status kvsel_prefill_chunk(const kvsel_heads* heads, const kvsel_batch* ba
     const Layout L = layout(s, true);
     if ((st = check_ws(workspace, workspace_bytes, L.total))) return st;
     return run_prefill(heads, batch, s, L, q, k_chunk, v_chunk, cache, out, out_dtype, idx, workspace,
+                       static_cast<hipStream_t>(stream));
+}
+
+kvsel_status kvsel_prefill_chunk_noalloc(const kvsel_heads* heads, const kvsel_batch* batch,
+                                         const kvsel_params* params, const void* q, const void* k_chunk,
+                                         const void* v_chunk, const kvsel_cache* cache, void* out,
+                                         int32_t out_dtype, int32_t* idx, void* stream) {
+    g_err.clear();
+    kvsel_status st;
+    int64_t t_max;
+    if ((st = check_prefill(heads, batch, params, q, k_chunk, v_chunk, cache, out_dtype, out, &t_max))) return st;
+    const SelShape s = make_shape(heads, batch, params, t_max);
+    if ((st = check_gather_rows(s, cache, heads, batch))) return st;
+    const Layout L = layout(s, true);
+    if (L.total > kNoAllocScratchBytes)
+        return fail(KVSEL_ERR_UNSUPPORTED, "these shapes need %zu bytes of workspace; the fixed scratch array holds %zu "
+                    "(use kvsel_prefill_chunk with a caller workspace)", L.total, kNoAllocScratchBytes);
+    void* ws = nullptr;
+    if ((st = scratch_address(&ws))) return st;
+    NoTraceScope no_trace;                        // trace events are created lazily: none on this path
+    return run_prefill(heads, batch, s, L, q, k_chunk, v_chunk, cache, out, out_dtype, idx, ws,
                        static_cast<hipStream_t>(stream));
 }
 

@@ -23,8 +23,8 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: 
 
 # the exported symbols of include/kvsel.h
 EXPORTS = ("kvsel_workspace_size", "kvsel_sparse_attn_workspace_size", "kvsel_select", "kvsel_sparse_attn",
-           "kvsel_prefill_chunk", "kvsel_compacted_view", "kvsel_last_error", "kvsel_version", "kvsel_trace_start",
-           "kvsel_trace_stop", "kvsel_trace_read", "kvsel_kernel_name")
+           "kvsel_prefill_chunk", "kvsel_prefill_chunk_noalloc", "kvsel_compacted_view", "kvsel_last_error",
+           "kvsel_version", "kvsel_trace_start", "kvsel_trace_stop", "kvsel_trace_read", "kvsel_kernel_name")
 KERNELS = ("qstats", "qtopk", "qpack", "scan", "topb", "gather", "pack", "attn", "append", "qpool")
 
 
@@ -73,9 +73,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvsel_select.argtypes = [P(Heads), P(Batch), P(Params), vp, P(Cache), vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kvsel_sparse_attn.argtypes = [P(Heads), P(Batch), vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, sz, vp]
     lib.kvsel_prefill_chunk.argtypes = [P(Heads), P(Batch), P(Params), vp, vp, vp, P(Cache), vp, i32, vp, vp, sz, vp]
+    lib.kvsel_prefill_chunk_noalloc.argtypes = [P(Heads), P(Batch), P(Params), vp, vp, vp, P(Cache), vp, i32, vp, vp]
     lib.kvsel_compacted_view.argtypes = [P(Heads), P(Batch), P(Params), P(Cache), P(i32), P(sz), P(sz), P(i32), P(i32)]
     for name in ("kvsel_workspace_size", "kvsel_sparse_attn_workspace_size", "kvsel_select", "kvsel_sparse_attn",
-                 "kvsel_prefill_chunk", "kvsel_compacted_view"):
+                 "kvsel_prefill_chunk", "kvsel_prefill_chunk_noalloc", "kvsel_compacted_view"):
         getattr(lib, name).restype = ctypes.c_int
     lib.kvsel_last_error.argtypes = []
     lib.kvsel_last_error.restype = ctypes.c_char_p
@@ -169,6 +170,14 @@ def kvsel_prefill_chunk(h: Heads, b: Batch, p: Params, q: torch.Tensor, k_chunk:
                                       k_chunk.data_ptr(), v_chunk.data_ptr(), ctypes.byref(c), out.data_ptr(),
                                       dtype_code(out), _ptr(idx), ws.data_ptr(), ws.numel() * ws.element_size(),
                                       _stream()))
+
+
+def kvsel_prefill_chunk_noalloc(h: Heads, b: Batch, p: Params, q: torch.Tensor, k_chunk: torch.Tensor,
+                                v_chunk: torch.Tensor, c: Cache, out: torch.Tensor,
+                                idx: Optional[torch.Tensor]) -> None:
+    _check(load().kvsel_prefill_chunk_noalloc(ctypes.byref(h), ctypes.byref(b), ctypes.byref(p), q.data_ptr(),
+                                              k_chunk.data_ptr(), v_chunk.data_ptr(), ctypes.byref(c),
+                                              out.data_ptr(), dtype_code(out), _ptr(idx), _stream()))
 
 
 def compacted_view(h: Heads, b: Batch, p: Params, c: Cache) -> Optional[dict]:

@@ -197,6 +197,24 @@ kvsel_status kvsel_prefill_chunk(const kvsel_heads *heads, const kvsel_batch *ba
                                  int32_t *idx, void *workspace, size_t workspace_bytes,
                                  void *stream);
 
+/* kvsel_prefill_chunk for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same computation and outputs as kvsel_prefill_chunk, with
+ * the workspace taken from a fixed device array inside the library instead of
+ * a caller buffer: KVSEL_NOALLOC_SCRATCH_BYTES per GPU, held from the first
+ * call on that GPU until the process ends.  Shapes whose workspace
+ * (kvsel_workspace_size) is larger return KVSEL_ERR_UNSUPPORTED with nothing
+ * enqueued.  The call allocates nothing (no hipMalloc / hipFree) and records
+ * no trace events.  Every call on one GPU uses that GPU's one array, which
+ * keeps the last call's contents: calls that overlap in time on one GPU (two
+ * streams, two threads) race on it and must be serialised by the caller. */
+#define KVSEL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kvsel_status kvsel_prefill_chunk_noalloc(const kvsel_heads *heads, const kvsel_batch *batch,
+                                         const kvsel_params *params, const void *q,
+                                         const void *k_chunk, const void *v_chunk,
+                                         const kvsel_cache *cache, void *out, int32_t out_dtype,
+                                         int32_t *idx, void *stream);
+
 /* Where kvsel_prefill_chunk leaves the compacted key list of step 4 in the
  * workspace, so that a caller can read it back after the call (QuoKA article,
  * Fig. 1(a): the compacted cache handed to attention).  For the shapes and
