@@ -282,6 +282,16 @@ Layout layout(const SelShape& s, bool with_attn) {
 // check_gather_rows: its workspace has no room for packed lists.)
 bool prefill_uses_gather(const SelShape& s) { return attn_use_gather(s); }
 
+// Whether kvsel_prefill_chunk attends to the cache prefix in place: nothing is
+// selected (every T_b <= budget, so the key list is cache rows [0, T_b) then
+// the chunk's rows, which the call appends at [T_b, T_b + C) first) and the
+// cache is contiguous; bf16 shapes of the packed attention, with the list's
+// byte size and the capacity within the kernel's 32-bit offsets.
+bool prefill_inplace(const SelShape& s, const kvsel_cache* c) {
+    return s.esz == 2 && !attn_use_gather(s) && c->block_size == 0 && s.t_max <= s.budget &&
+           (s.t_max + s.C) * s.d * 2 < (int64_t(1) << 31) && c->capacity < (int64_t(1) << 31) / (s.d * 2);
+}
+
 kvsel_status check_gather_rows(const SelShape& s, const kvsel_cache* c, const kvsel_heads* h, const kvsel_batch* b) {
     if (attn_use_gather(s) && !cache_rows_fit(c, h, b))
         return fail(KVSEL_ERR_UNSUPPORTED, "chunks of %d tokens x %d query heads per KV head read the cache through "
@@ -385,6 +395,16 @@ kvsel_status run_prefill(const kvsel_heads* heads, const kvsel_batch* batch, con
         KVSEL_TRY(traced(KVSEL_K_ATTN, hs, [&] { return launch_attn(s, q, nullptr, nullptr, nullptr, 0, scale, out, out_dtype == KVSEL_F32,
                               at<float>(workspace, L.apart), hs, &ga); }), "attention");
         KVSEL_TRY(traced(KVSEL_K_APPEND, hs, [&] { return launch_append(s, cv, batch->prior_len_dev, k_chunk, v_chunk, hs); }), "cache append");
+        return KVSEL_OK;
+    }
+    if (prefill_inplace(s, cache)) {
+        // nothing selected: append the chunk, then the key list of every
+        // (sequence, KV head) is its cache rows [0, T_b + C), read in place
+        KVSEL_TRY(traced(KVSEL_K_APPEND, hs, [&] { return launch_append(s, cv, batch->prior_len_dev, k_chunk, v_chunk, hs); }), "cache append");
+        AttnGather ga{cv, batch->prior_len_dev, s.budget, nullptr, 0, k_chunk, v_chunk};
+        KVSEL_TRY(traced(KVSEL_K_ATTN, hs, [&] { return launch_attn(s, q, cache->k, cache->v, nullptr, static_cast<int>(cache->capacity), scale,
+                                                                    out, out_dtype == KVSEL_F32, at<float>(workspace, L.apart), hs, &ga, true); }),
+                  "attention");
         return KVSEL_OK;
     }
     KVSEL_TRY(traced(KVSEL_K_PACK, hs, [&] { return launch_pack(s, src, k_chunk, v_chunk, L.nk_pad, at<void>(workspace, L.kall), at<void>(workspace, L.vall),
@@ -497,7 +517,7 @@ kvsel_status kvsel_compacted_view(const kvsel_heads* heads, const kvsel_batch* b
     const SelShape s = make_shape(heads, batch, params, t_max);
     const Layout L = layout(s, true);
     if ((st = check_gather_rows(s, cache, heads, batch))) return st;
-    *packed = prefill_uses_gather(s) ? 0 : 1;
+    *packed = (prefill_uses_gather(s) || prefill_inplace(s, cache)) ? 0 : 1;
     *k_offset = L.kall;
     *v_offset = L.vall;
     *slots = L.nk_pad;

@@ -9,6 +9,7 @@
 // (token, head-in-group) rows of all G heads of a KV head and stages each key
 // tile in LDS once for all of them.  Multi-query attention page, "Teknisk
 // innsikt": each query head uses its own query against the shared K/V.
+#include <algorithm>
 #include <type_traits>
 
 #include "launch.h"
@@ -55,7 +56,12 @@ constexpr int kAttnKT = 64;           // keys per staged tile
 // GATHER: the key list is read from its sources (kept cache rows through idx,
 // then the chunk's rows) instead of the packed copy; V then arrives row-major
 // and is staged [key][d], its V^T fragments read with LDS transpose loads.
-template <int D, bool OUT_F32, int KT, int WAVES, bool GATHER>
+// INPLACE: every prior key is kept (T_b <= budget) and the chunk's rows have
+// been appended to a contiguous cache, so rows [0, T_b + C) of the cache are
+// the key list itself: kall / vall are the cache's K and V ([b][g][nk_pad][d],
+// nk_pad = capacity), read in place (V row-major as with GATHER); loads past
+// row T_b + C return zeros (the cache beyond is not part of the list).
+template <int D, bool OUT_F32, int KT, int WAVES, bool GATHER, bool INPLACE>
 __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ kall,
                                                            const uint16_t* __restrict__ vall,
@@ -63,7 +69,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
                                                            int h_kv, int row_blocks, float cl2,
                                                            void* __restrict__ out, int ksplit,
                                                            float* __restrict__ part, AttnGather ga, int cu_pair) {
-    constexpr bool VR = GATHER;             // V tile staged row-major
+    static_assert(!(GATHER && INPLACE), "one key-list source");
+    constexpr bool VR = GATHER || INPLACE;  // V tile staged row-major
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
     constexpr int NKB = KT / 32;            // 32-key MFMA blocks per tile
@@ -102,8 +109,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
     }
     const int b = bg / h_kv, g = bg % h_kv;
     const int nrows = G * C;
-    const int64_t T_b = GATHER ? ga.prior_len[b] : 0;
-    const int n_s = GATHER ? static_cast<int>(T_b < ga.budget ? T_b : ga.budget) : nsel[b];
+    const int64_t T_b = (GATHER || INPLACE) ? ga.prior_len[b] : 0;
+    const int n_s = (GATHER || INPLACE) ? static_cast<int>(T_b < ga.budget ? T_b : ga.budget) : nsel[b];
     const int row_wg0 = rblk * ROWS;
     const int wg_tmax = min(row_wg0 + ROWS - 1, nrows - 1) / G;
     const int ntiles_all = (n_s + wg_tmax + 1 + KT - 1) / KT;
@@ -142,7 +149,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
     if constexpr (GATHER) complete_q();
 
     const uint16_t* kb = kall + static_cast<int64_t>(bg) * nk_pad * D;
-    const uint16_t* vb = vall + static_cast<int64_t>(bg) * D * nk_pad;
+    const uint16_t* vb = vall + static_cast<int64_t>(bg) * D * nk_pad;   // [d][slot] packed, [row][d] in place
     // Staging with a full tile of latency for every load (t counts tiles in
     // the order this workgroup reads them): V(t+1) is fetched at the start of
     // tile t and written to LDS at its end; K(t+1), fetched in the middle of
@@ -164,10 +171,12 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
         const int p = tid + NT * i;
         voff[i] = static_cast<uint32_t>(((p / (KT / 8)) * nk_pad + (p % (KT / 8)) * 8) * 2);
     }
-    // buffer descriptors over this KV head's packed K and V^T (reads past the
-    // end return 0); the tile offset is the uniform soffset operand
-    const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kb), 0, nk_pad * D * 2, kBufferFormat);
-    const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vb), 0, nk_pad * D * 2, kBufferFormat);
+    // buffer descriptors over this KV head's packed K and V^T, or its cache
+    // rows [0, T_b + C) in place (reads past the end return 0); the tile
+    // offset is the uniform soffset operand
+    const int list_bytes = (INPLACE ? n_s + C : nk_pad) * D * 2;
+    const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kb), 0, list_bytes, kBufferFormat);
+    const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vb), 0, list_bytes, kBufferFormat);
     // the tile index is the same in every lane; readfirstlane hands it to the
     // scalar offset operand directly (no per-lane waterfall over its values)
     auto fetch_k = [&](int t) {
@@ -208,9 +217,15 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
         }
     };
     auto fetch_v = [&](int t) {
-        const int so = __builtin_amdgcn_readfirstlane(t * KT * 2);
+        if constexpr (INPLACE) {              // row-major rows, the same pieces as K
+            const int so = __builtin_amdgcn_readfirstlane(t * KT * D * 2);
 #pragma unroll
-        for (int i = 0; i < PV; ++i) rv[i] = __builtin_amdgcn_raw_buffer_load_b128(rsv, voff[i], so, 0);
+            for (int i = 0; i < PV; ++i) rv[i] = __builtin_amdgcn_raw_buffer_load_b128(rsv, koff[i], so, 0);
+        } else {
+            const int so = __builtin_amdgcn_readfirstlane(t * KT * 2);
+#pragma unroll
+            for (int i = 0; i < PV; ++i) rv[i] = __builtin_amdgcn_raw_buffer_load_b128(rsv, voff[i], so, 0);
+        }
     };
     auto stash_v = [&](int buf) {
 #pragma unroll
@@ -868,13 +883,15 @@ static bool attn_use_pp(const SelShape& s) {
     return wgs < 256 || wgs >= 512;
 }
 
-int attn_ksplit(const SelShape& s) {
+int attn_ksplit(const SelShape& s, bool inplace) {
     if (s.esz != 2) return 1;
     // gathering workgroups wait on dependent loads (index, block table, row):
     // four shorter key ranges per row block keep more of them in flight
     if (attn_use_gather(s)) return 4;
     // at least two 4-wave workgroups, or one 8-wave ping-pong workgroup, per CU
-    const int rows = attn_use_pp(s) ? 256 : 128, target = attn_use_pp(s) ? 256 : 512;
+    // (the in-place list is read by the 4-wave kernel only)
+    const bool pp = !inplace && attn_use_pp(s);
+    const int rows = pp ? 256 : 128, target = pp ? 256 : 512;
     const int64_t wgs = int64_t(s.batch) * s.h_kv * ((s.G * s.C + rows - 1) / rows);
     int k = 1;
     while (k < 4 && wgs * k < target) k *= 2;
@@ -882,7 +899,7 @@ int attn_ksplit(const SelShape& s) {
 }
 
 size_t attn_part_bytes(const SelShape& s) {
-    const int k = attn_ksplit(s);
+    const int k = std::max(attn_ksplit(s, false), attn_ksplit(s, true));
     if (k == 1) return 0;
     const size_t rows = size_t(s.batch) * s.h_q * s.C;
     return size_t(k) * rows * (s.d + 2) * 4;
@@ -890,28 +907,34 @@ size_t attn_part_bytes(const SelShape& s) {
 
 hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const void* vall, const int32_t* nsel,
                        int nk_pad, float scale, void* out, bool out_f32, float* part, hipStream_t st,
-                       const AttnGather* gather) {
+                       const AttnGather* gather, bool inplace) {
     const int bgs = s.batch * s.h_kv;
     if (s.esz == 2) {
-        const bool pp = !gather && attn_use_pp(s);             // 8 waves x 32 rows, else 4 waves
+        // with inplace, `gather` only carries the prior lengths and the budget
+        const bool gathering = gather && !inplace;
+        const bool pp = !gather && attn_use_pp(s);                // 8 waves x 32 rows, else 4 waves
         const int row_blocks = (s.G * s.C + (pp ? 255 : 127)) / (pp ? 256 : 128);
-        const int ksplit = attn_ksplit(s);
+        const int ksplit = attn_ksplit(s, inplace);
         dim3 grid(bgs * row_blocks * ksplit), block(pp ? 512 : 256);
         // 4-wave packed kernel in one round of two workgroups per CU, whole KV
         // heads per XCD: pair long with short row blocks on each CU
         const int64_t per_xcd = grid.x / kXcds;
-        const int cu_pair = (!gather && !pp && ksplit == 1 && row_blocks > 1 &&
+        const int cu_pair = (!gathering && !pp && ksplit == 1 && row_blocks > 1 &&
                              grid.x % kXcds == 0 && per_xcd % row_blocks == 0 &&
                              int64_t(grid.x) <= 2 * int64_t(device_cus())) ? 1 : 0;
         const float cl2 = scale * 1.4426950408889634f;
         const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)kall, *vv = (const uint16_t*)vall;
         const AttnGather ga = gather ? *gather : AttnGather{};
-#define KVSEL_ATTN(D, F32, W) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, kAttnKT, W, false>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part, ga, cu_pair)
-#define KVSEL_ATTN_G(D, F32) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, kAttnKT, 4, true>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part, ga, 0)
+#define KVSEL_ATTN(D, F32, W) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, kAttnKT, W, false, false>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part, ga, cu_pair)
+#define KVSEL_ATTN_I(D, F32) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, kAttnKT, 4, false, true>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part, ga, cu_pair)
+#define KVSEL_ATTN_G(D, F32) hipLaunchKernelGGL((attn_mfma_kernel<D, F32, kAttnKT, 4, true, false>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part, ga, 0)
 #define KVSEL_ATTN_PPK(D, F32) hipLaunchKernelGGL((attn_pp_kernel<D, F32>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, cl2, out, ksplit, part)
-        if (gather) {
+        if (gathering) {
             if (s.d == 128) { if (out_f32) KVSEL_ATTN_G(128, true); else KVSEL_ATTN_G(128, false); }
             else { if (out_f32) KVSEL_ATTN_G(64, true); else KVSEL_ATTN_G(64, false); }
+        } else if (inplace) {
+            if (s.d == 128) { if (out_f32) KVSEL_ATTN_I(128, true); else KVSEL_ATTN_I(128, false); }
+            else { if (out_f32) KVSEL_ATTN_I(64, true); else KVSEL_ATTN_I(64, false); }
         } else if (pp) {
             if (out_f32) KVSEL_ATTN_PPK(128, true); else KVSEL_ATTN_PPK(128, false);
         } else if (s.d == 128) {
@@ -920,6 +943,7 @@ hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const
             if (out_f32) KVSEL_ATTN(64, true, 4); else KVSEL_ATTN(64, false, 4);
         }
 #undef KVSEL_ATTN
+#undef KVSEL_ATTN_I
 #undef KVSEL_ATTN_G
 #undef KVSEL_ATTN_PPK
         if (ksplit > 1) {

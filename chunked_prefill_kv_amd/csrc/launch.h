@@ -157,11 +157,16 @@ bool attn_use_gather(const SelShape& s);
 // CU (gathering: always) the key tiles of every row block are split over
 // attn_ksplit(s) workgroups whose partials (fp32 scratch `part` of
 // attn_part_bytes(s) bytes) a merge kernel combines.
-int attn_ksplit(const SelShape& s);
+// With inplace (every prior key kept, contiguous cache, the chunk already
+// appended): kall / vall are the cache's K / V and nk_pad its capacity; the key
+// list of (b, g) is cache rows [0, T_b + C) read in place, n_b = T_b from
+// gather->prior_len (gather->budget >= every T_b); the 4-wave kernel runs it.
+int attn_ksplit(const SelShape& s, bool inplace = false);
 size_t attn_part_bytes(const SelShape& s);
 hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const void* vall,
                        const int32_t* nsel, int nk_pad, float scale, void* out, bool out_f32,
-                       float* part, hipStream_t st, const AttnGather* gather = nullptr);
+                       float* part, hipStream_t st, const AttnGather* gather = nullptr,
+                       bool inplace = false);
 
 // Cache append without packing: chunk rows -> cache rows [T_b, T_b + C).
 hipError_t launch_append(const SelShape& s, const CacheView& cv, const int64_t* prior_len, const void* k_chunk,

@@ -221,7 +221,10 @@ kvsel_status kvsel_prefill_chunk_noalloc(const kvsel_heads *heads, const kvsel_b
  * cache given (only its layout is read):
  *   *packed = 1 when the call builds the lists in the workspace, 0 when its
  *     attention reads the kept rows in place (no lists; the other outputs are
- *     then left unwritten);
+ *     then left unwritten): through their cache row numbers (chunks of G x
+ *     chunk_len <= 128 query rows per KV head), or, when no sequence selects
+ *     (every T_b <= budget) on a contiguous bf16 cache, as the cache prefix
+ *     [0, T_b) followed by the chunk's rows, which the call appends first;
  *   keys at byte offset *k_offset: [batch][h_kv][*slots][d] (one row per slot);
  *   values at *v_offset: [batch][h_kv][d][*slots] (transposed) when
  *     *v_transposed, else [batch][h_kv][*slots][d];

@@ -568,3 +568,53 @@ def test_topb_boundary_bin_over_capacity(dup):
     n = B
     assert np.array_equal(runner.to_host_bits(ks[0, 0])[:n], keys[idx_h[:n]])
     assert np.array_equal(runner.to_host_bits(vs[0, 0])[:n], vcache[0, 0, idx_h[:n]])
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_prefill_in_place_when_nothing_selected(d):
+    """When no sequence selects (every T_b <= B) on a contiguous cache, the call
+    appends the chunk and attends to the cache prefix in place (no compacted
+    copy).  Ragged prior lengths including 0; the cache rows past each
+    sequence's T_b + C hold NaN, so any read beyond the key list would show in
+    O.  Every sequence against the oracle with every prior key kept."""
+    C, Ts, B = 200, [0, 200, 600, 450], 600
+    wl = LLAMA.replace(L=max(Ts) + C, C=C, H_q=8, H_kv=2, d=d, n_q=24, B=B)
+    print(f"[case] in-place prefill d={d} T={Ts}", flush=True)
+    nb, cap = len(Ts), max(Ts) + C + 64
+    cur = [gen.chunk_inputs(wl, T // C if T % C == 0 else 0, seq=s) for s, T in enumerate(Ts)]
+    rng = np.random.default_rng([0x5EED, 991, d])
+    nan = np.uint16(0x7FC0)
+    kc = np.full((nb, wl.H_kv, cap, wl.d), nan, dtype=np.uint16)
+    vc = np.full_like(kc, nan)
+    for s, T in enumerate(Ts):
+        kc[s, :, :T] = gen.f32_to_bf16_bits(rng.standard_normal((wl.H_kv, T, wl.d)).astype(np.float32))
+        vc[s, :, :T] = gen.f32_to_bf16_bits(rng.standard_normal((wl.H_kv, T, wl.d)).astype(np.float32))
+    dev = "cuda"
+    kc_d, vc_d = runner.to_device(kc, dev), runner.to_device(vc, dev)
+    q = runner.to_device(np.stack([c[0] for c in cur]), dev)
+    kn = runner.to_device(np.stack([c[1] for c in cur]), dev)
+    vn = runner.to_device(np.stack([c[2] for c in cur]), dev)
+    h = K.heads(wl.H_q, wl.H_kv, wl.d, K.KVSEL_BF16)
+    p = K.Params(wl.n_q, wl.B)
+    prior_d = torch.tensor(Ts, dtype=torch.int64, device=dev)
+    b = K.batch(Ts, C, prior_d)
+    cache = K.cache(kc_d, vc_d, cap)
+    assert K.compacted_view(h, b, p, cache) is None, "expected the in-place attention (no compacted lists)"
+    ws = torch.empty(K.workspace_size(h, b, p), dtype=torch.uint8, device=dev)
+    out = torch.empty(nb, wl.H_q, C, wl.d, dtype=torch.float32, device=dev)
+    idx = torch.full((nb, wl.H_kv, B), -7, dtype=torch.int32, device=dev)
+    K.kvsel_prefill_chunk(h, b, p, q, kn, vn, cache, out, idx, ws)
+    torch.cuda.synchronize()
+    kc_after, vc_after = runner.to_host_bits(kc_d), runner.to_host_bits(vc_d)
+    O = out.double().cpu().numpy()
+    idx_h = idx.cpu().numpy()
+    assert not np.isnan(O).any(), "a NaN row past the key list was read"
+    for s, T in enumerate(Ts):
+        assert np.array_equal(kc_after[s, :, T:T + C], cur[s][1]) and np.array_equal(vc_after[s, :, T:T + C], cur[s][2])
+        assert np.array_equal(kc_after[s, :, :T], kc[s, :, :T]) and np.array_equal(kc_after[s, :, T + C:], kc[s, :, T + C:])
+        for g in range(wl.H_kv):
+            assert np.array_equal(idx_h[s, g, :T], np.arange(T)) and np.all(idx_h[s, g, T:] == -1)
+        Qc, Kn, Vn = (gen.to_f64(x) for x in cur[s])
+        Kp, Vp = gen.to_f64(kc[s, :, :T]), gen.to_f64(vc[s, :, :T])
+        O_or = quoka.attend(Qc, [Kp[g] for g in range(wl.H_kv)], [Vp[g] for g in range(wl.H_kv)], Kn, Vn)
+        parity.check_close(O[s], O_or, parity.o_tol(wl.dtype), f"O seq {s}")
