@@ -117,3 +117,28 @@ def prefill(chunks, n_q: int, B: int, scale: float | None = None, pooling: str =
             Kp[g] = Kp[g] + [list(r) for r in Kc[g]]
             Vp[g] = Vp[g] + [list(r) for r in Vc[g]]
     return out
+
+
+def reuse_slots(prev_pos: Sequence[int], idx: Sequence[int]) -> List[int]:
+    """Slot contents after a decode step that selected idx (ascending), by the
+    selected-entry cache rule (SQD page, sparse-attention paragraph; the
+    reading in oracle/reuse.py): walk the slots in order, keep a slot below
+    n = len(idx) whose position is selected again, then hand the remaining
+    selected positions, smallest first, to the remaining slots below n,
+    lowest first; slots from n on are empty (-1)."""
+    n = len(idx)
+    selected = set(idx)
+    new = [-1] * len(prev_pos)
+    taken = set()
+    for s in range(n):
+        p = prev_pos[s]
+        if p >= 0 and p in selected and p not in taken:
+            new[s] = p
+            taken.add(p)
+    waiting = [p for p in idx if p not in taken]
+    w = 0
+    for s in range(n):
+        if new[s] == -1:
+            new[s] = waiting[w]
+            w += 1
+    return new
