@@ -158,6 +158,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=8,
+                    help="decode workload: consecutive steps of the reuse measurement")
     ap.add_argument("--lib", default=None, help="path of an alternative libkvsel.so build")
     ap.add_argument("--pooling", choices=["head", "group"], default="head",
                     help="order of the score poolings: per-head max then group mean (default), or group-pooled rows first")
@@ -277,7 +279,7 @@ def bench_decode(args):
     K.load(args.lib) if args.lib else K.load()
     wl = gen.WORKLOADS[args.workload]
     print(f"[bench] generating {wl.name} inputs", file=sys.stderr, flush=True)
-    di = gen.decode_inputs(wl)
+    di = gen.decode_inputs(wl, steps=args.decode_steps)
     dr = runner.DecodeRunner(wl, di, out_dtype=torch.bfloat16)
     for _ in range(args.warmup):
         dr.run()
@@ -314,10 +316,48 @@ def bench_decode(args):
                         "launches": n_sc, "avg_launch_us": round(ms_sc * 1e3 / n_sc, 2)},
            "kernels": {k: {"ms_per_step": round(v[1] / args.steps, 4)} for k, v in tr.items()},
            "cpu_baseline": None}
+    del dr
+    out["reuse"] = bench_decode_reuse(wl, di, args.decode_steps)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on the decode step", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline_decode(wl, di)
     print(json.dumps(out), flush=True)
+
+
+def bench_decode_reuse(wl, di, S):
+    """S consecutive decode steps (the generator's tokens at T_b .. T_b + S - 1), plain and
+    with the selected-entry cache (kvsel_decode_reuse; its first step fills the cache):
+    time per step over steps 1 .. S-1 of each, and the hit rate of those steps."""
+    import torch
+    from chunked_prefill_kv_amd import runner
+    sr = runner.DecodeStepsRunner(wl, di)
+    st = torch.cuda.current_stream()
+    ms = {}
+    for reuse in (False, True):
+        for _ in range(2):                       # the second pass is timed
+            sr.reset()
+            sr.step(0, reuse)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for t in range(1, S):
+                sr.step(t, reuse)
+            e1.record(st)
+            torch.cuda.synchronize()
+        ms["reuse" if reuse else "plain"] = e0.elapsed_time(e1) / (S - 1)
+    sr.reset()
+    hits = kept = 0
+    for t in range(S):
+        sr.step(t, True)
+        torch.cuda.synchronize()
+        if t:
+            c = sr.counts.cpu().numpy()
+            hits += int(c[..., 0].sum())
+            kept += int(c.sum())
+    return {"steps": S, "ms_per_step_plain": round(ms["plain"], 4), "ms_per_step_reuse": round(ms["reuse"], 4),
+            "hit_rate": round(hits / max(kept, 1), 4),
+            "what": "steps 1..S-1 of S consecutive decode steps; hit = a kept entry already in the "
+                    "selected-entry cache from the previous step (its rows are not fetched again)"}
 
 
 if __name__ == "__main__":

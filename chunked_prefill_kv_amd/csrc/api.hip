@@ -58,8 +58,8 @@ constexpr int64_t kMaxLen = int64_t(1) << 30;   // positions fit int32 kernel ar
 
 // ----------------------------------------------------------------------------- tracing
 
-const char* const kKernelNames[KVSEL_K_COUNT] = {"qstats", "qtopk", "qpack", "scan", "topb",
-                                                 "gather", "pack", "attn", "append", "qpool"};
+const char* const kKernelNames[KVSEL_K_COUNT] = {"qstats", "qtopk", "qpack", "scan", "topb", "gather",
+                                                 "pack", "attn", "append", "qpool", "reuse"};
 
 struct Trace {
     std::mutex mu;
@@ -613,6 +613,48 @@ kvsel_status kvsel_prefill_chunk(const kvsel_heads* heads, const kvsel_batch* ba
     if ((st = check_ws(workspace, workspace_bytes, L.total))) return st;
     return run_prefill(heads, batch, s, L, q, k_chunk, v_chunk, cache, out, out_dtype, idx, workspace,
                        static_cast<hipStream_t>(stream));
+}
+
+kvsel_status kvsel_decode_reuse(const kvsel_heads* heads, const kvsel_batch* batch, const kvsel_params* params,
+                                const void* q, const void* k_new, const void* v_new, const kvsel_cache* cache,
+                                const kvsel_sel_cache* sel, void* out, int32_t out_dtype, int32_t* idx,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    g_err.clear();
+    kvsel_status st;
+    int64_t t_max;
+    if ((st = check_prefill(heads, batch, params, q, k_new, v_new, cache, out_dtype, out, &t_max))) return st;
+    if (!sel || !sel->k || !sel->v || !sel->pos) return fail(KVSEL_ERR_INVALID_ARG, "sel / sel->k / sel->v / sel->pos is NULL");
+    if (!aligned16(sel->k) || !aligned16(sel->v)) return fail(KVSEL_ERR_INVALID_ARG, "sel->k / sel->v must be 16-byte aligned");
+    if (heads->dtype != KVSEL_BF16) return fail(KVSEL_ERR_UNSUPPORTED, "the selected-entry cache is implemented for bf16");
+    if (params->budget > kReuseMaxBudget)
+        return fail(KVSEL_ERR_UNSUPPORTED, "budget=%d: the selected-entry cache holds at most %d slots", params->budget, kReuseMaxBudget);
+    const SelShape s = make_shape(heads, batch, params, t_max);
+    if (!attn_use_gather(s))
+        return fail(KVSEL_ERR_UNSUPPORTED, "decode reuse needs (h_q / h_kv) * chunk_len <= 128 (got %d)", s.G * s.C);
+    if ((st = check_gather_rows(s, cache, heads, batch))) return st;
+    if (int64_t(s.batch) * s.h_kv * s.budget >= (int64_t(1) << 31))
+        return fail(KVSEL_ERR_UNSUPPORTED, "the selected-entry cache holds 2^31 slots or more");
+    const Layout L = layout(s, true);
+    if ((st = check_ws(workspace, workspace_bytes, L.total))) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const CacheView cv = make_view(cache, heads);
+    int32_t* idx_buf = idx ? idx : at<int32_t>(workspace, L.idx);
+    if ((st = run_select(s, batch, q, cv, workspace, L, idx_buf, nullptr, nullptr, hs))) return st;
+    KVSEL_TRY(traced(KVSEL_K_REUSE, hs, [&] { return launch_reuse(s, cv, batch->prior_len_dev, idx_buf, sel->k, sel->v, sel->pos,
+                                                                  sel->counts, hs); }), "selected-entry cache update");
+    // the slot buffer as a contiguous cache of `budget` rows per (sequence, KV head)
+    CacheView sv = cv;
+    sv.k = static_cast<char*>(sel->k);
+    sv.v = static_cast<char*>(sel->v);
+    sv.capacity = s.budget;
+    sv.block_size = 0;
+    sv.block_table = nullptr;
+    AttnGather ga{sv, batch->prior_len_dev, s.budget, nullptr, s.budget, k_new, v_new, 1};
+    const float scale = heads->scale > 0.0f ? heads->scale : 1.0f / std::sqrt(static_cast<float>(heads->d));
+    KVSEL_TRY(traced(KVSEL_K_ATTN, hs, [&] { return launch_attn(s, q, nullptr, nullptr, nullptr, 0, scale, out, out_dtype == KVSEL_F32,
+                                                                at<float>(workspace, L.apart), hs, &ga); }), "attention");
+    KVSEL_TRY(traced(KVSEL_K_APPEND, hs, [&] { return launch_append(s, cv, batch->prior_len_dev, k_new, v_new, hs); }), "cache append");
+    return KVSEL_OK;
 }
 
 kvsel_status kvsel_prefill_chunk_noalloc(const kvsel_heads* heads, const kvsel_batch* batch,

@@ -194,7 +194,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
 #pragma unroll
         for (int i = 0; i < PK; ++i) {
             const int sl = t * KT + (tid + NT * i) / (D / 8);
-            rr[i] = sl < n_s ? ga.rowidx[static_cast<int64_t>(bg) * ga.ri_stride + sl]
+            rr[i] = sl < n_s ? (ga.identity ? static_cast<int32_t>(bg * ga.ri_stride + sl)
+                                            : ga.rowidx[static_cast<int64_t>(bg) * ga.ri_stride + sl])
                              : -1 - (bg * C + min(sl - n_s, C - 1));
         }
     };

@@ -146,7 +146,21 @@ struct AttnGather {
     int64_t ri_stride;
     const void* k_chunk;             // [b][h_kv][C][d]
     const void* v_chunk;
+    // slot s of (b, g) is row (b * h_kv + g) * ri_stride + s of cv (a contiguous
+    // slot buffer, the selected-entry cache); rowidx is then not read
+    int identity;
 };
+
+// Cross-step reuse of the selected entries (decode): after the top-B wrote idx
+// (ascending, n_b = min(budget, T_b) per (b, g)), update the slot buffer
+// sel_k / sel_v [b][g][budget][d] and its positions pos [b][g][budget]: a slot
+// below n_b whose position is selected again keeps it, the other selected
+// positions (misses, ascending) fill the remaining slots below n_b (ascending)
+// and their rows are copied from the cache; slots from n_b on become -1.
+// counts (optional) [b][g][2]: hits, misses.  budget <= kReuseMaxBudget.
+constexpr int kReuseMaxBudget = 8192;
+hipError_t launch_reuse(const SelShape& s, const CacheView& cv, const int64_t* prior_len, const int32_t* idx,
+                        void* sel_k, void* sel_v, int32_t* pos, int32_t* counts, hipStream_t st);
 // bf16 KV heads with a single 128-row block (G * C <= 128: decode, short
 // chunks) take the gathering attention: each key row is read by one workgroup
 // only, so packing it first is pure extra traffic.

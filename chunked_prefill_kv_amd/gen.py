@@ -241,6 +241,11 @@ class DecodeInputs:
     block_table: np.ndarray        # [batch][max_blocks] int32 (physical block ids; -1 unused)
     k_pool: np.ndarray             # [num_blocks][H_kv][block][d] (prior tokens filled, rest 0)
     v_pool: np.ndarray
+    # consecutive steps (decode_inputs(..., steps=S)): step t is the token at
+    # position T_b + t; step 0 is q / k_new / v_new above
+    q_steps: Optional[np.ndarray] = None       # [S][batch][H_q][1][d]
+    k_steps: Optional[np.ndarray] = None       # [S][batch][H_kv][1][d]
+    v_steps: Optional[np.ndarray] = None
 
     def logical_kv(self, b: int, block_size: int) -> Tuple[np.ndarray, np.ndarray]:
         """Prior K, V of sequence b as [H_kv][T_b][d] read back from the pool (layout helper)."""
@@ -256,12 +261,14 @@ def decode_lengths(wl: Workload) -> np.ndarray:
     return _rng(wl.wid, TAG_LEN).integers(wl.decode_len_lo, wl.decode_len_hi + 1, size=wl.batch).astype(np.int64)
 
 
-def decode_inputs(wl: Workload, lengths: Optional[np.ndarray] = None) -> DecodeInputs:
-    """Ragged decode step: sequence b has T_b prior tokens in a paged pool and one new token at T_b."""
+def decode_inputs(wl: Workload, lengths: Optional[np.ndarray] = None, steps: int = 1) -> DecodeInputs:
+    """Ragged decode step: sequence b has T_b prior tokens in a paged pool and one new token at T_b.
+    With steps = S the pool has room for S new tokens per sequence and q_steps / k_steps /
+    v_steps hold the generator's tokens at positions T_b .. T_b + S - 1 (consecutive steps)."""
     bs = wl.block_size
     lens = decode_lengths(wl) if lengths is None else np.asarray(lengths, dtype=np.int64)
     batch = len(lens)
-    nblk = [(int(t) + 1 + bs - 1) // bs for t in lens]          # room for the new token too
+    nblk = [(int(t) + steps + bs - 1) // bs for t in lens]      # room for the new tokens too
     total = int(sum(nblk))
     perm = _rng(wl.wid, TAG_PERM).permutation(total).astype(np.int32)
     maxb = max(nblk)
@@ -273,14 +280,14 @@ def decode_inputs(wl: Workload, lengths: Optional[np.ndarray] = None) -> DecodeI
     store = np.uint16 if wl.dtype == "bf16" else np.float32
     k_pool = np.zeros((total, wl.H_kv, bs, wl.d), dtype=store)
     v_pool = np.zeros((total, wl.H_kv, bs, wl.d), dtype=store)
-    q = np.empty((batch, wl.H_q, 1, wl.d), dtype=store)
-    k_new = np.empty((batch, wl.H_kv, 1, wl.d), dtype=store)
-    v_new = np.empty((batch, wl.H_kv, 1, wl.d), dtype=store)
+    q_s = np.empty((steps, batch, wl.H_q, 1, wl.d), dtype=store)
+    k_s = np.empty((steps, batch, wl.H_kv, 1, wl.d), dtype=store)
+    v_s = np.empty((steps, batch, wl.H_kv, 1, wl.d), dtype=store)
     for b in range(batch):
         T = int(lens[b])
         for g in range(wl.H_kv):
-            kk = _finish(_k_rows_f32(wl, g, b, 0, T + 1), wl.dtype)
-            vv = _finish(_v_rows_f32(wl, g, b, 0, T + 1), wl.dtype)
+            kk = _finish(_k_rows_f32(wl, g, b, 0, T + steps), wl.dtype)
+            vv = _finish(_v_rows_f32(wl, g, b, 0, T + steps), wl.dtype)
             padded = nblk[b] * bs
             kp = np.zeros((padded, wl.d), dtype=store)
             vp = np.zeros((padded, wl.d), dtype=store)
@@ -288,11 +295,12 @@ def decode_inputs(wl: Workload, lengths: Optional[np.ndarray] = None) -> DecodeI
             vp[:T] = vv[:T]
             k_pool[table[b, : nblk[b]], g] = kp.reshape(nblk[b], bs, wl.d)
             v_pool[table[b, : nblk[b]], g] = vp.reshape(nblk[b], bs, wl.d)
-            k_new[b, g, 0] = kk[T]
-            v_new[b, g, 0] = vv[T]
+            k_s[:, b, g, 0] = kk[T:T + steps]
+            v_s[:, b, g, 0] = vv[T:T + steps]
         for h in range(wl.H_q):
-            q[b, h, 0] = _finish(_q_rows_f32(wl, h, b, T, 1), wl.dtype)[0]
-    return DecodeInputs(lens, q, k_new, v_new, table, k_pool, v_pool)
+            q_s[:, b, h, 0] = _finish(_q_rows_f32(wl, h, b, T, steps), wl.dtype)
+    return DecodeInputs(lens, q_s[0].copy(), k_s[0].copy(), v_s[0].copy(), table, k_pool, v_pool,
+                        q_s if steps > 1 else None, k_s if steps > 1 else None, v_s if steps > 1 else None)
 
 
 def describe(wl: Workload) -> dict:

@@ -23,9 +23,10 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: 
 
 # the exported symbols of include/kvsel.h
 EXPORTS = ("kvsel_workspace_size", "kvsel_sparse_attn_workspace_size", "kvsel_select", "kvsel_sparse_attn",
-           "kvsel_prefill_chunk", "kvsel_prefill_chunk_noalloc", "kvsel_compacted_view", "kvsel_last_error",
+           "kvsel_prefill_chunk", "kvsel_prefill_chunk_noalloc", "kvsel_decode_reuse", "kvsel_compacted_view",
+           "kvsel_last_error",
            "kvsel_version", "kvsel_trace_start", "kvsel_trace_stop", "kvsel_trace_read", "kvsel_kernel_name")
-KERNELS = ("qstats", "qtopk", "qpack", "scan", "topb", "gather", "pack", "attn", "append", "qpool")
+KERNELS = ("qstats", "qtopk", "qpack", "scan", "topb", "gather", "pack", "attn", "append", "qpool", "reuse")
 
 
 class Heads(ctypes.Structure):
@@ -42,6 +43,11 @@ class Cache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("capacity", ctypes.c_int64),
                 ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("block_table", ctypes.c_void_p)]
+
+
+class SelCache(ctypes.Structure):
+    """The selected-entry cache of kvsel_decode_reuse (device pointers)."""
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("counts", ctypes.c_void_p)]
 
 
 class Batch(ctypes.Structure):
@@ -73,10 +79,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvsel_select.argtypes = [P(Heads), P(Batch), P(Params), vp, P(Cache), vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kvsel_sparse_attn.argtypes = [P(Heads), P(Batch), vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, sz, vp]
     lib.kvsel_prefill_chunk.argtypes = [P(Heads), P(Batch), P(Params), vp, vp, vp, P(Cache), vp, i32, vp, vp, sz, vp]
+    lib.kvsel_decode_reuse.argtypes = [P(Heads), P(Batch), P(Params), vp, vp, vp, P(Cache), P(SelCache), vp, i32, vp, vp,
+                                       sz, vp]
     lib.kvsel_prefill_chunk_noalloc.argtypes = [P(Heads), P(Batch), P(Params), vp, vp, vp, P(Cache), vp, i32, vp, vp]
     lib.kvsel_compacted_view.argtypes = [P(Heads), P(Batch), P(Params), P(Cache), P(i32), P(sz), P(sz), P(i32), P(i32)]
     for name in ("kvsel_workspace_size", "kvsel_sparse_attn_workspace_size", "kvsel_select", "kvsel_sparse_attn",
-                 "kvsel_prefill_chunk", "kvsel_prefill_chunk_noalloc", "kvsel_compacted_view"):
+                 "kvsel_prefill_chunk", "kvsel_prefill_chunk_noalloc", "kvsel_decode_reuse", "kvsel_compacted_view"):
         getattr(lib, name).restype = ctypes.c_int
     lib.kvsel_last_error.argtypes = []
     lib.kvsel_last_error.restype = ctypes.c_char_p
@@ -170,6 +178,20 @@ def kvsel_prefill_chunk(h: Heads, b: Batch, p: Params, q: torch.Tensor, k_chunk:
                                       k_chunk.data_ptr(), v_chunk.data_ptr(), ctypes.byref(c), out.data_ptr(),
                                       dtype_code(out), _ptr(idx), ws.data_ptr(), ws.numel() * ws.element_size(),
                                       _stream()))
+
+
+def sel_cache(k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor, counts: Optional[torch.Tensor] = None) -> SelCache:
+    c = SelCache(k.data_ptr(), v.data_ptr(), pos.data_ptr(), _ptr(counts))
+    c._keep = (k, v, pos, counts)    # raw pointers in the struct: keep the tensors alive with it
+    return c
+
+
+def kvsel_decode_reuse(h: Heads, b: Batch, p: Params, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                       c: Cache, sel: SelCache, out: torch.Tensor, idx: Optional[torch.Tensor], ws: torch.Tensor) -> None:
+    _check(load().kvsel_decode_reuse(ctypes.byref(h), ctypes.byref(b), ctypes.byref(p), q.data_ptr(), k_new.data_ptr(),
+                                     v_new.data_ptr(), ctypes.byref(c), ctypes.byref(sel), out.data_ptr(),
+                                     dtype_code(out), _ptr(idx), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                     _stream()))
 
 
 def kvsel_prefill_chunk_noalloc(h: Heads, b: Batch, p: Params, q: torch.Tensor, k_chunk: torch.Tensor,

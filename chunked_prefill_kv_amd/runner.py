@@ -104,3 +104,49 @@ class DecodeRunner:
     def run(self) -> None:
         K.kvsel_prefill_chunk(self.h, self.b, self.p, self.q, self.k_new, self.v_new, self.cache, self.out,
                               self.idx, self.ws)
+
+
+class DecodeStepsRunner:
+    """Consecutive decode steps of a ragged paged batch (step t: the token at T_b + t),
+    either plain (kvsel_prefill_chunk) or with the selected-entry cache
+    (kvsel_decode_reuse).  `inputs` must come from gen.decode_inputs(..., steps=S)."""
+
+    def __init__(self, wl: gen.Workload, inputs: gen.DecodeInputs, device="cuda", out_dtype=torch.bfloat16):
+        assert inputs.q_steps is not None, "decode_inputs(..., steps=S) with S > 1"
+        self.wl = wl
+        self.S = inputs.q_steps.shape[0]
+        self.device = device
+        self.k_pool = to_device(inputs.k_pool, device)
+        self.v_pool = to_device(inputs.v_pool, device)
+        self.table = to_device(inputs.block_table, device)
+        self.q = [to_device(x, device) for x in inputs.q_steps]
+        self.k_new = [to_device(x, device) for x in inputs.k_steps]
+        self.v_new = [to_device(x, device) for x in inputs.v_steps]
+        self.h = K.heads(wl.H_q, wl.H_kv, wl.d, K.KVSEL_BF16)
+        self.p = K.Params(wl.n_q, wl.B)
+        T0 = inputs.prior_len.astype(np.int64)
+        self.prior = [torch.tensor(T0 + t, dtype=torch.int64, device=device) for t in range(self.S)]
+        self.batches = [K.batch((T0 + t).tolist(), 1, self.prior[t]) for t in range(self.S)]
+        self.cache = K.cache(self.k_pool, self.v_pool, self.k_pool.shape[0], wl.block_size, self.table)
+        self.ws = torch.empty(max(K.workspace_size(self.h, b, self.p) for b in self.batches), dtype=torch.uint8,
+                              device=device)
+        nb = len(T0)
+        self.out = torch.empty(nb, wl.H_q, 1, wl.d, dtype=out_dtype, device=device)
+        self.idx = torch.empty(nb, wl.H_kv, wl.B, dtype=torch.int32, device=device)
+        self.sel_k = torch.empty(nb, wl.H_kv, wl.B, wl.d, dtype=torch.bfloat16, device=device)
+        self.sel_v = torch.empty_like(self.sel_k)
+        self.pos = torch.full((nb, wl.H_kv, wl.B), -1, dtype=torch.int32, device=device)
+        self.counts = torch.zeros(nb, wl.H_kv, 2, dtype=torch.int32, device=device)
+        self.sel = K.sel_cache(self.sel_k, self.sel_v, self.pos, self.counts)
+
+    def reset(self) -> None:
+        """Empty the selected-entry cache (a new sequence per batch entry)."""
+        self.pos.fill_(-1)
+
+    def step(self, t: int, reuse: bool) -> None:
+        if reuse:
+            K.kvsel_decode_reuse(self.h, self.batches[t], self.p, self.q[t], self.k_new[t], self.v_new[t], self.cache,
+                                 self.sel, self.out, self.idx, self.ws)
+        else:
+            K.kvsel_prefill_chunk(self.h, self.batches[t], self.p, self.q[t], self.k_new[t], self.v_new[t],
+                                  self.cache, self.out, self.idx, self.ws)

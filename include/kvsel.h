@@ -197,6 +197,46 @@ kvsel_status kvsel_prefill_chunk(const kvsel_heads *heads, const kvsel_batch *ba
                                  int32_t *idx, void *workspace, size_t workspace_bytes,
                                  void *stream);
 
+/* The selected-entry cache of decode with cross-step reuse (SQD page,
+ * rit.work, the paragraph on sparse attention: the top-k selection scans the
+ * whole cache each step, the values at the selected positions are kept from
+ * one step to the next and only the misses are fetched).  The page gives no
+ * slot policy; the one used: after a step's top-B (n_b = min(budget, T_b)
+ * positions per KV head), a slot below n_b whose position is selected again
+ * keeps its rows (a hit); the selected positions held by no such slot (the
+ * misses), in ascending order, are fetched from the KV cache into the other
+ * slots below n_b, in ascending order; slots from n_b on become empty.
+ * Caller-owned device memory, kept from one call to the next:
+ *   k, v     [batch][h_kv][budget][d], element type heads->dtype
+ *   pos      [batch][h_kv][budget] int32: the position each slot holds, -1 =
+ *            empty.  Set every entry to -1 before a sequence's first step (and
+ *            when a batch entry starts another sequence); after that only the
+ *            library writes it.
+ *   counts   optional [batch][h_kv][2] int32: hits and misses of the last call */
+typedef struct {
+    void *k, *v;
+    int32_t *pos;
+    int32_t *counts;
+} kvsel_sel_cache;
+
+#define KVSEL_REUSE_MAX_BUDGET 8192
+
+/* One decode step of every sequence (chunk_len tokens each, with
+ * (h_q / h_kv) * chunk_len <= 128) with the selected-entry cache `sel`:
+ * steps 1-3 as in kvsel_prefill_chunk, then the update of `sel` above, then
+ * attention of every query over the slots [0, n_b) of its KV head plus the
+ * step's own tokens (causal), then the cache append at [T_b, T_b + chunk_len).
+ * The output is kvsel_prefill_chunk's up to floating-point summation order
+ * (softmax attention does not depend on the order of its keys; QuoKA
+ * article, Fig. 1(a)).  bf16 only; budget <= KVSEL_REUSE_MAX_BUDGET;
+ * workspace as sized by kvsel_workspace_size.  idx: optional out as in
+ * kvsel_select.  Errors: as kvsel_select. */
+kvsel_status kvsel_decode_reuse(const kvsel_heads *heads, const kvsel_batch *batch,
+                                const kvsel_params *params, const void *q, const void *k_new,
+                                const void *v_new, const kvsel_cache *cache, const kvsel_sel_cache *sel,
+                                void *out, int32_t out_dtype, int32_t *idx, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
 /* kvsel_prefill_chunk for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  The same computation and outputs as kvsel_prefill_chunk, with
@@ -258,7 +298,8 @@ typedef enum {
     KVSEL_K_ATTN = 7,     /* step 5: attention */
     KVSEL_K_APPEND = 8,   /* cache append on its own (gathering attention path; otherwise inside the pack kernel) */
     KVSEL_K_QPOOL = 9,    /* step 1 with KVSEL_POOL_GROUP: the group's unit queries averaged per token */
-    KVSEL_K_COUNT = 10
+    KVSEL_K_REUSE = 10,   /* kvsel_decode_reuse: slot update and miss fetch of the selected-entry cache */
+    KVSEL_K_COUNT = 11
 } kvsel_kernel;
 
 kvsel_status kvsel_trace_start(uint32_t kernel_mask);

@@ -142,3 +142,22 @@ def test_compacted_view_host_arithmetic():
     b1 = K.batch([4096] * 4, 1, None)
     b1.prior_len_dev = 256
     assert K.compacted_view(h, b1, K.Params(1, 2048), K.Cache(fake, fake, 8192, 0, 0, None)) is None
+
+
+def test_decode_reuse_rejects_on_host():
+    """kvsel_decode_reuse: NULL selected-entry cache, fp32, a budget above 8192 and
+    a chunk too long for the gathering attention are refused before any launch."""
+    lib, fake = K.load(), 1 << 20
+    c = K.Cache(fake, fake, 4096, 16, 512, fake)
+    sel = K.SelCache(fake, fake, fake, None)
+
+    def call(h, b, p, s):
+        b.prior_len_dev = 256
+        return lib.kvsel_decode_reuse(ctypes.byref(h), ctypes.byref(b), ctypes.byref(p), fake, fake, fake,
+                                      ctypes.byref(c), s, fake, K.KVSEL_F32, None, fake, 1 << 40, None)
+    h, p = K.heads(32, 8, 128, K.KVSEL_BF16), K.Params(1, 2048)
+    assert call(h, K.batch([5000] * 4, 1, None), p, None) == K.KVSEL_ERR_INVALID_ARG
+    assert call(K.heads(32, 8, 128, K.KVSEL_F32), K.batch([5000] * 4, 1, None), p, ctypes.byref(sel)) == K.KVSEL_ERR_UNSUPPORTED
+    assert call(h, K.batch([5000] * 4, 1, None), K.Params(1, 9000), ctypes.byref(sel)) == K.KVSEL_ERR_UNSUPPORTED
+    assert call(h, K.batch([5000] * 4, 64, None), p, ctypes.byref(sel)) == K.KVSEL_ERR_UNSUPPORTED
+    assert "128" in K.last_error()
