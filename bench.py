@@ -105,7 +105,8 @@ def host_cpu():
 def cpu_baseline(wl, chunks, pooling="head"):
     """The oracle, as it stands, on the same inputs: the whole prompt for prompts of
     up to 16 chunks (the 32K layer: about 40 s of host work), else every 8th chunk
-    (the last of each group of 8) over the full prior cache."""
+    (the last of each group of 8; every 16th when a chunk holds more than 2048 x 32
+    query rows) over the full prior cache."""
     from chunked_prefill_kv_amd import gen
     from oracle import quoka
     cores, model = host_cpu()
@@ -117,7 +118,8 @@ def cpu_baseline(wl, chunks, pooling="head"):
         tokens = sum(c[0].shape[1] for c in c64)
         what = f"the whole {len(chunks)}-chunk prompt"
     else:
-        ks = list(range(7, len(chunks), 8))
+        every = 16 if wl.C * wl.H_q > 2048 * 32 else 8
+        ks = list(range(every - 1, len(chunks), every))
         tokens, t_total = 0, 0.0
         for k in ks:
             Qc, Kc, Vc = c64[k]
