@@ -215,8 +215,11 @@ __global__ __launch_bounds__(256) void scan_rows16_kernel(const uint16_t* __rest
                                                          int64_t s_stride) {
     constexpr int KS = D / 32;          // k-steps of 32
     constexpr int KEYS = 4 * GROUPS * 16;
-    const int slot = xcd_slot(blockIdx.x, gridDim.x);
-    const int bg = slot / tiles, tile = slot % tiles;
+    // slots follow the launch order, so every XCD receives an even share of
+    // the key tiles whatever the sequence lengths (grouping a sequence's tiles
+    // on one XCD, as the prefill scan does for L2 reuse, buys nothing here:
+    // every key is read once)
+    const int bg = blockIdx.x / tiles, tile = blockIdx.x % tiles;
     const int b = bg / h_kv, g = bg % h_kv;
     const int64_t T = prior_len[b];
     if (T <= budget) return;
