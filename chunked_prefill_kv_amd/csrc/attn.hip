@@ -798,43 +798,56 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
 
 // ----------------------------------------------------------------------------- fp32 VALU kernel
 //
-// One thread per query row, key/value tiles of 32 rows staged in LDS and
-// shared by the 128 rows of the workgroup.
+// 16 lanes per query row, each holding D/16 consecutive elements of q and of
+// the output; a workgroup takes 16 rows ((token, head-in-group) pairs as in
+// the MFMA kernels) and stages 32-key tiles of K and V in LDS.  Each lane
+// forms its part of q . k, the 16 lanes of the row add their parts with DPP,
+// and every lane runs the row's online softmax and accumulates its slice of
+// P.V.
 template <int D, bool OUT_F32>
-__global__ __launch_bounds__(128) void attn_valu_kernel(const float* __restrict__ q, const float* __restrict__ kall,
+__global__ __launch_bounds__(256) void attn_valu_kernel(const float* __restrict__ q, const float* __restrict__ kall,
                                                         const float* __restrict__ vall,
                                                         const int32_t* __restrict__ nsel, int nk_pad, int C, int G,
                                                         int h_kv, int row_blocks, float scale,
                                                         void* __restrict__ out) {
     constexpr int KT = 32;
-    __shared__ float qs[128][D + 1];
-    __shared__ float kt[KT][D];
-    __shared__ float vt[KT][D];
+    constexpr int DPL = D / 16;             // elements per lane
+    constexpr int RPW = 16;                 // rows per workgroup
+    constexpr int PPT = KT * D / 4 / 256;   // float4 pieces per thread per tile
+    __shared__ __attribute__((aligned(16))) float kt[KT][D];
+    __shared__ __attribute__((aligned(16))) float vt[KT][D];
     const int bg = blockIdx.x / row_blocks;
     const int rblk = row_blocks - 1 - blockIdx.x % row_blocks;
     const int b = bg / h_kv, g = bg % h_kv;
     const int nrows = G * C;
     const int n_s = nsel[b];
-    const int row0 = rblk * 128;
-    const int wg_tmax = min(row0 + 127, nrows - 1) / G;
+    const int row0 = rblk * RPW;
+    const int wg_tmax = min(row0 + RPW - 1, nrows - 1) / G;
     const int ntiles = (n_s + wg_tmax + 1 + KT - 1) / KT;
-    const int qrow = row0 + threadIdx.x;
+    const int c = threadIdx.x & 15;
+    const int qrow = row0 + (threadIdx.x >> 4);
     const bool rvalid = qrow < nrows;
     const int tok = rvalid ? qrow / G : 0, hh = rvalid ? qrow % G : 0;
     const int64_t qoff = ((static_cast<int64_t>(b) * h_kv * G + g * G + hh) * C + tok) * D;
-    for (int e = 0; e < D; ++e) qs[threadIdx.x][e] = rvalid ? q[qoff + e] : 0.0f;
+    float qv[DPL], acc[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; e += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(q + qoff + c * DPL + e);
+        qv[e] = x[0]; qv[e + 1] = x[1]; qv[e + 2] = x[2]; qv[e + 3] = x[3];
+    }
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
     const float* kb = kall + static_cast<int64_t>(bg) * nk_pad * D;
     const float* vb = vall + static_cast<int64_t>(bg) * nk_pad * D;
-    float acc[D];
-#pragma unroll
-    for (int e = 0; e < D; ++e) acc[e] = 0.0f;
     float m = -INFINITY, l = 0.0f;
-    const int lim = n_s + tok;
+    const int lim = n_s + tok;                  // slot 0 is always visible, so m is finite after tile 0
     for (int t = 0; t < ntiles; ++t) {
         __syncthreads();
-        for (int i = threadIdx.x; i < KT * D; i += 128) {
-            kt[i / D][i % D] = kb[static_cast<int64_t>(t) * KT * D + i];
-            vt[i / D][i % D] = vb[static_cast<int64_t>(t) * KT * D + i];
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int p = threadIdx.x + 256 * i;
+            reinterpret_cast<f32x4*>(&kt[0][0])[p] = reinterpret_cast<const f32x4*>(kb + static_cast<int64_t>(t) * KT * D)[p];
+            reinterpret_cast<f32x4*>(&vt[0][0])[p] = reinterpret_cast<const f32x4*>(vb + static_cast<int64_t>(t) * KT * D)[p];
         }
         __syncthreads();
         float s[KT];
@@ -843,7 +856,8 @@ __global__ __launch_bounds__(128) void attn_valu_kernel(const float* __restrict_
         for (int j = 0; j < KT; ++j) {
             float dot = 0.0f;
 #pragma unroll
-            for (int e = 0; e < D; ++e) dot = fmaf(qs[threadIdx.x][e], kt[j][e], dot);
+            for (int e = 0; e < DPL; ++e) dot = fmaf(qv[e], kt[j][c * DPL + e], dot);
+            dot = row16_sum(dot);
             s[j] = (t * KT + j <= lim) ? dot * scale : -INFINITY;
             mt = fmaxf(mt, s[j]);
         }
@@ -851,21 +865,22 @@ __global__ __launch_bounds__(128) void attn_valu_kernel(const float* __restrict_
         const float alpha = expf(m - m_new);
         l *= alpha;
 #pragma unroll
-        for (int e = 0; e < D; ++e) acc[e] *= alpha;
+        for (int e = 0; e < DPL; ++e) acc[e] *= alpha;
         m = m_new;
 #pragma unroll
         for (int j = 0; j < KT; ++j) {
             const float p = expf(s[j] - m);
             l += p;
 #pragma unroll
-            for (int e = 0; e < D; ++e) acc[e] = fmaf(p, vt[j][e], acc[e]);
+            for (int e = 0; e < DPL; ++e) acc[e] = fmaf(p, vt[j][c * DPL + e], acc[e]);
         }
     }
     if (!rvalid) return;
     const float inv = 1.0f / l;
-    for (int e = 0; e < D; ++e) {
-        if (OUT_F32) static_cast<float*>(out)[qoff + e] = acc[e] * inv;
-        else static_cast<uint16_t*>(out)[qoff + e] = f32_to_bf16(acc[e] * inv);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+        if (OUT_F32) static_cast<float*>(out)[qoff + c * DPL + e] = acc[e] * inv;
+        else static_cast<uint16_t*>(out)[qoff + c * DPL + e] = f32_to_bf16(acc[e] * inv);
     }
 }
 
@@ -959,15 +974,15 @@ hipError_t launch_attn(const SelShape& s, const void* q, const void* kall, const
             }
         }
     } else {
-        const int row_blocks = (s.G * s.C + 127) / 128;
-        dim3 grid(bgs * row_blocks);
+        const int row_blocks = (s.G * s.C + 15) / 16;
+        dim3 grid(bgs * row_blocks), block(256);
         const float *qq = (const float*)q, *kk = (const float*)kall, *vv = (const float*)vall;
         if (s.d == 128) {
-            if (out_f32) hipLaunchKernelGGL((attn_valu_kernel<128, true>), grid, dim3(128), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, scale, out);
-            else hipLaunchKernelGGL((attn_valu_kernel<128, false>), grid, dim3(128), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, scale, out);
+            if (out_f32) hipLaunchKernelGGL((attn_valu_kernel<128, true>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, scale, out);
+            else hipLaunchKernelGGL((attn_valu_kernel<128, false>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, scale, out);
         } else {
-            if (out_f32) hipLaunchKernelGGL((attn_valu_kernel<64, true>), grid, dim3(128), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, scale, out);
-            else hipLaunchKernelGGL((attn_valu_kernel<64, false>), grid, dim3(128), 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, scale, out);
+            if (out_f32) hipLaunchKernelGGL((attn_valu_kernel<64, true>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, scale, out);
+            else hipLaunchKernelGGL((attn_valu_kernel<64, false>), grid, block, 0, st, qq, kk, vv, nsel, nk_pad, s.C, s.G, s.h_kv, row_blocks, scale, out);
         }
     }
     return hipGetLastError();

@@ -34,16 +34,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return static_cast<uint16_t>(pack_bf16x2(f, 0.0f) & 0xFFFFu);
 }
 
-template <typename T> struct Elem;
-template <> struct Elem<float> {
-    static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
-    static constexpr int bytes = 4;
-};
-template <> struct Elem<uint16_t> {
-    static __device__ __forceinline__ float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
-    static constexpr int bytes = 2;
-};
-
 // ---------------------------------------------------------------- cache addressing
 
 // Where row `pos` of sequence b, KV head g lives (contiguous or paged cache).
@@ -88,6 +78,20 @@ __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
     return x;
+}
+
+// Sum over the 16 lanes of each DPP row (lanes 16r .. 16r+15); every lane of
+// the row receives the total.  Rotations by 8 and 4 inside the row, then swaps
+// of lane pairs 2 and 1 apart inside each group of four.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x = dpp_add<0x128>(x);     // row_ror:8
+    x = dpp_add<0x124>(x);     // row_ror:4
+    x = dpp_add<0x4E>(x);      // quad_perm [2,3,0,1]
+    return dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]
 }
 
 // Order-preserving map fp32 -> uint32 (larger float -> larger key); -0 is

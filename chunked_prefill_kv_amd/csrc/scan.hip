@@ -284,35 +284,47 @@ __global__ __launch_bounds__(256) void scan_rows16_kernel(const uint16_t* __rest
     }
 }
 
-// ----------------------------------------------------------------------------- generic VALU scan (fp32 inputs)
-
-template <typename E, int D>
-__global__ __launch_bounds__(256) void scan_valu_kernel(const E* __restrict__ qsel, const float* __restrict__ rq,
+// ----------------------------------------------------------------------------- VALU scan (fp32 inputs)
+//
+// 16 lanes per key, each holding D/16 consecutive elements of the key row; a
+// workgroup scores 16 keys.  The kept query rows of the KV head pass through
+// LDS in stages of 32; each lane forms its part of q . k and the 16 lanes of
+// the key add their parts with DPP (every lane gets the dot product), so the
+// max over a head's queries and the mean over the heads run in every lane.
+template <int D>
+__global__ __launch_bounds__(256) void scan_valu_kernel(const float* __restrict__ qsel, const float* __restrict__ rq,
                                                         CacheView cv, const int64_t* __restrict__ prior_len,
                                                         int64_t budget, int h_kv, int G, int nqp, int tiles,
                                                         float* __restrict__ S, int64_t s_stride) {
-    constexpr int QR = 32;
-    __shared__ float qs[QR][D];
+    constexpr int DPL = D / 16;             // elements per lane
+    constexpr int KPW = 16;                 // keys per workgroup
+    constexpr int QR = 32;                  // query rows per LDS stage
+    __shared__ __attribute__((aligned(16))) float qs[QR][D];
     __shared__ float rqs[QR];
     const int bg = blockIdx.x / tiles, tile = blockIdx.x % tiles;
     const int b = bg / h_kv, g = bg % h_kv;
     const int64_t T = prior_len[b];
     if (T <= budget) return;
-    const int64_t key0 = static_cast<int64_t>(tile) * 256;
+    const int64_t key0 = static_cast<int64_t>(tile) * KPW;
     if (key0 >= T) return;
-    const int64_t key = key0 + threadIdx.x;
-    const bool valid = key < T;
-    float k[D];
+    const int c = threadIdx.x & 15;
+    const int64_t key = key0 + (threadIdx.x >> 4);
+    const bool valid = key < T;             // lanes past T score row 0 and write nothing
+    float k[DPL];
     {
-        const E* row = reinterpret_cast<const E*>(cv.k + (valid ? cv.row_offset(b, g, key) : 0));
+        const float* row = reinterpret_cast<const float*>(cv.k + (valid ? cv.row_offset(b, g, key) : cv.row_offset(b, g, 0)));
 #pragma unroll
-        for (int e = 0; e < D; ++e) k[e] = valid ? Elem<E>::load(row, e) : 0.0f;
+        for (int e = 0; e < DPL; e += 4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(row + c * DPL + e);
+            k[e] = x[0]; k[e + 1] = x[1]; k[e + 2] = x[2]; k[e + 3] = x[3];
+        }
     }
     float n2 = 0.0f;
 #pragma unroll
-    for (int e = 0; e < D; ++e) n2 = fmaf(k[e], k[e], n2);
+    for (int e = 0; e < DPL; ++e) n2 = fmaf(k[e], k[e], n2);
+    n2 = row16_sum(n2);
     const float rkv = n2 > 0.0f ? 1.0f / sqrtf(n2) : 0.0f;
-    const E* qb = qsel + static_cast<int64_t>(bg) * G * nqp * D;
+    const float* qb = qsel + static_cast<int64_t>(bg) * G * nqp * D;
     const float* rqb = rq + static_cast<int64_t>(bg) * G * nqp;
     float sum = 0.0f;
     for (int hh = 0; hh < G; ++hh) {
@@ -320,20 +332,21 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const E* __restrict__ qs
         for (int r0 = 0; r0 < nqp; r0 += QR) {
             const int nr = min(QR, nqp - r0);
             __syncthreads();
-            for (int i = threadIdx.x; i < nr * D; i += 256)
-                qs[i / D][i % D] = Elem<E>::load(qb, (static_cast<int64_t>(hh) * nqp + r0) * D + i);
+            for (int i = threadIdx.x; i < nr * D / 4; i += 256)
+                reinterpret_cast<f32x4*>(&qs[0][0])[i] =
+                    reinterpret_cast<const f32x4*>(qb + (static_cast<int64_t>(hh) * nqp + r0) * D)[i];
             if (threadIdx.x < nr) rqs[threadIdx.x] = rqb[hh * nqp + r0 + threadIdx.x];
             __syncthreads();
             for (int r = 0; r < nr; ++r) {
                 float dot = 0.0f;
 #pragma unroll
-                for (int e = 0; e < D; ++e) dot = fmaf(qs[r][e], k[e], dot);
-                run = fmaxf(run, dot * rqs[r]);
+                for (int e = 0; e < DPL; ++e) dot = fmaf(qs[r][c * DPL + e], k[e], dot);
+                run = fmaxf(run, row16_sum(dot) * rqs[r]);
             }
         }
         sum += run;
     }
-    if (valid) S[static_cast<int64_t>(bg) * s_stride + key] = sum * (1.0f / static_cast<float>(G)) * rkv;
+    if (valid && c == 0) S[static_cast<int64_t>(bg) * s_stride + key] = sum * (1.0f / static_cast<float>(G)) * rkv;
 }
 
 // ----------------------------------------------------------------------------- launcher
@@ -381,10 +394,10 @@ hipError_t launch_scan(const SelShape& s, const void* qsel, const float* rq, con
         }
 #undef KVSEL_SCAN
     } else {
-        const int tiles = static_cast<int>((s.t_max + 255) / 256);
+        const int tiles = static_cast<int>((s.t_max + 15) / 16);
         dim3 grid(bgs * tiles), block(256);
-        if (s.d == 128) hipLaunchKernelGGL((scan_valu_kernel<float, 128>), grid, block, 0, st, (const float*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, S, s_stride);
-        else hipLaunchKernelGGL((scan_valu_kernel<float, 64>), grid, block, 0, st, (const float*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, S, s_stride);
+        if (s.d == 128) hipLaunchKernelGGL((scan_valu_kernel<128>), grid, block, 0, st, (const float*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, S, s_stride);
+        else hipLaunchKernelGGL((scan_valu_kernel<64>), grid, block, 0, st, (const float*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, s.nq_pad, tiles, S, s_stride);
     }
     return hipGetLastError();
 }

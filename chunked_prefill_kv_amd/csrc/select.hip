@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     __shared__ uint32_t hist[kHistBins];
     __shared__ uint32_t wsum[kTopkWaves];
     __shared__ uint32_t wtot[2][kTopkWaves];
-    __shared__ uint32_t s_digit, s_rem;
+    __shared__ uint32_t s_digit, s_rem, s_full;
 
     // bits shared by every key need no histogram pass
     const uint32_t first = gkey(0);
@@ -302,6 +302,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
             if (above < remaining && above + hb[i] >= remaining) {
                 s_digit = BPT * t + i;
                 s_rem = remaining - above;
+                s_full = remaining - above == hb[i] ? 1u : 0u;   // every key of the bin is kept
             }
             above += hb[i];
         }
@@ -309,9 +310,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
         prefix |= s_digit << shift;
         remaining = s_rem;
         bits = shift;
+        if (s_full && bits > 0 && prefix > 0) {
+            // the kept keys are exactly those >= prefix (the bin's lowest key):
+            // no further digits are needed, tau sits just below the bin and
+            // no key equal to it is kept
+            prefix -= 1;
+            remaining = 0;
+            bits = 0;
+        }
         __syncthreads();
     }
-    const uint32_t tau = prefix;          // the k-th largest key
+    const uint32_t tau = prefix;          // the k-th largest key (or just below the kept range)
     const uint32_t need = remaining;      // keys equal to tau that are kept (lowest indices)
 
     // Ordered compaction: wave w owns the contiguous segment [w*seg, (w+1)*seg).

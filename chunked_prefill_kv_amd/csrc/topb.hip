@@ -117,7 +117,7 @@ __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
     __shared__ int cj[kCap];
     __shared__ uint32_t sgt[kTopbMaxSegments], seq_[kTopbMaxSegments];   // per-segment counts
     __shared__ uint32_t wsum[16];
-    __shared__ uint32_t s_bin, s_need, s_cnt, s_digit, s_rem;
+    __shared__ uint32_t s_bin, s_need, s_cnt, s_digit, s_rem, s_full;
     const float* c = a.comb + static_cast<int64_t>(p) * a.s_stride;
     // the pass's first scores are requested before the histogram, so they
     // arrive while the boundary bin is found; each later step's scores are
@@ -227,12 +227,26 @@ __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
         const int t = 1023 - tid;
         const uint32_t h0 = hs[2 * t], h1 = hs[2 * t + 1];
         const uint32_t above = excl_scan_1024(h0 + h1, wsum);
-        if (above < remaining && above + h1 >= remaining) { s_digit = 2 * t + 1; s_rem = remaining - above; }
-        else if (above + h1 < remaining && above + h1 + h0 >= remaining) { s_digit = 2 * t; s_rem = remaining - above - h1; }
+        if (above < remaining && above + h1 >= remaining) {
+            s_digit = 2 * t + 1;
+            s_rem = remaining - above;
+            s_full = remaining - above == h1 ? 1u : 0u;          // every key of the bin is kept
+        } else if (above + h1 < remaining && above + h1 + h0 >= remaining) {
+            s_digit = 2 * t;
+            s_rem = remaining - above - h1;
+            s_full = remaining - above - h1 == h0 ? 1u : 0u;
+        }
         __syncthreads();
         prefix |= s_digit << shift;
         remaining = s_rem;
         bits = shift;
+        if (s_full && bits > 0 && prefix > 0) {
+            // the kept boundary keys are exactly those >= prefix: tau sits just
+            // below them and no key equal to it is kept
+            prefix -= 1;
+            remaining = 0;
+            bits = 0;
+        }
         __syncthreads();
     }
     const uint32_t tau = prefix, need_eq = remaining;
