@@ -22,7 +22,7 @@ namespace {
 constexpr int kBins = 4096;
 constexpr int kSeg = kTopbSegKeys;   // keys per segment (one workgroup of 256 threads, 8 keys each)
 static_assert(kSeg == 8 * 256, "a segment is 8 keys per thread of a 256-thread workgroup");
-constexpr int kCap = 8192;        // boundary-bin keys kept in LDS by topb_thresh
+constexpr int kCap = 6144;        // boundary-bin keys kept in LDS by topb_thresh
 
 __device__ __forceinline__ int value_bin(float v) {
     const float f = floorf((v + 1.0f) * 2048.0f);
@@ -299,13 +299,16 @@ __global__ __launch_bounds__(256) void topb_write_kernel(TopbArgs a) {
     if (j0 >= T) return;
     const uint32_t tau = a.thr[2 * p], need_eq = a.thr[2 * p + 1];
     const uint32_t* sc = a.segc + static_cast<int64_t>(p) * a.nseg * 2;
-    __shared__ uint32_t wcnt[2][4];
-    __shared__ uint32_t base_gt, base_eq;
-    if (threadIdx.x == 0) {                    // kept keys in earlier segments
+    __shared__ uint32_t wcnt[2][4], wbase[2][4];
+    {                                          // kept keys in earlier segments, summed by all threads
         uint32_t g = 0, e = 0;
-        for (int s = 0; s < seg; ++s) { g += sc[2 * s]; e += sc[2 * s + 1]; }
-        base_gt = g;
-        base_eq = e;
+        for (int s = threadIdx.x; s < seg; s += 256) { g += sc[2 * s]; e += sc[2 * s + 1]; }
+#pragma unroll
+        for (int o2 = 32; o2 >= 1; o2 >>= 1) {
+            g += __shfl_xor(g, o2, kWave);
+            e += __shfl_xor(e, o2, kWave);
+        }
+        if (lane == 0) { wbase[0][wave] = g; wbase[1][wave] = e; }
     }
     uint32_t u[8];
     bool in[8];
@@ -322,7 +325,8 @@ __global__ __launch_bounds__(256) void topb_write_kernel(TopbArgs a) {
     }
     if (lane == 0) { wcnt[0][wave] = ng; wcnt[1][wave] = ne; }
     __syncthreads();
-    uint32_t gt_run = base_gt, eq_run = base_eq;
+    uint32_t gt_run = wbase[0][0] + wbase[0][1] + wbase[0][2] + wbase[0][3];
+    uint32_t eq_run = wbase[1][0] + wbase[1][1] + wbase[1][2] + wbase[1][3];
     for (int w = 0; w < wave; ++w) { gt_run += wcnt[0][w]; eq_run += wcnt[1][w]; }
     const uint64_t lt = (1ull << lane) - 1ull;
 #pragma unroll
