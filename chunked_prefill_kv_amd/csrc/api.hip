@@ -332,7 +332,7 @@ kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, 
         KVSEL_TRY(traced(KVSEL_K_QTOPK, st, [&] { return launch_topk(s.batch * s.h_kv, s.h_kv, at<float>(ws, L.qcos), s.C, 1, 0, nullptr, T, s.C, s.budget, s.nqp, keep, s.nqp,
                               1, s.C, st); }), "query top-k");
         KVSEL_TRY(traced(KVSEL_K_QPACK, st, [&] { return launch_pack_pooled(sc, qbar, keep, s.nqp, T, at<void>(ws, L.qsel), at<float>(ws, L.rq), st); }), "query packing");
-        KVSEL_TRY(traced(KVSEL_K_SCAN, st, [&] { return launch_scan(sc, at<void>(ws, L.qsel), at<float>(ws, L.rq), cv, T, S, s.t_max, st); }), "key scan");
+        KVSEL_TRY(traced(KVSEL_K_SCAN, st, [&] { return launch_scan(sc, at<void>(ws, L.qsel), at<float>(ws, L.rq), cv, T, S, s.t_max, st, b->prior_len_host); }), "key scan");
     } else if (any) {
         int32_t* keep = q_keep ? q_keep : at<int32_t>(ws, L.keep);
         const bool keep_all = s.nqp == s.C;   // every query kept: no statistics to take (decode)
@@ -344,7 +344,7 @@ kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, 
         KVSEL_TRY(traced(KVSEL_K_QPACK, st, [&] { return launch_pack_qsel(s, q, keep, s.nqp, at<float>(ws, L.qrn), T, at<void>(ws, L.qsel), at<float>(ws, L.rq), st,
                                                                          keep_all, at<uint32_t>(ws, L.topb), int64_t(s.batch) * s.h_kv * 4096); }),
                   "query packing");
-        KVSEL_TRY(traced(KVSEL_K_SCAN, st, [&] { return launch_scan(s, at<void>(ws, L.qsel), at<float>(ws, L.rq), cv, T, S, s.t_max, st); }), "key scan");
+        KVSEL_TRY(traced(KVSEL_K_SCAN, st, [&] { return launch_scan(s, at<void>(ws, L.qsel), at<float>(ws, L.rq), cv, T, S, s.t_max, st, b->prior_len_host); }), "key scan");
     }
     float* comb = scores ? scores : S;
     KVSEL_TRY(traced(KVSEL_K_TOPB, st, [&] { return launch_topb(s.batch * s.h_kv, s.h_kv, S, sc.nsplit, split_stride, comb, s.t_max, T,

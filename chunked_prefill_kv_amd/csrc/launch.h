@@ -102,8 +102,11 @@ hipError_t launch_pack_pooled(const SelShape& sp, const float* qbar, const int32
 // Step 2: S[b][g][j] for j < T_b (sequences with T_b > budget only).  With
 // s.nsplit > 1 the MFMA scan writes s.nsplit partial arrays, split k at
 // S + k * (batch * h_kv * s_stride), whose sum is the score.
+// prior_len_host (optional): the prior lengths on the host; the one-query scan
+// then launches only the workgroups that have keys to score
 hipError_t launch_scan(const SelShape& s, const void* qsel, const float* rq, const CacheView& cv,
-                       const int64_t* prior_len, float* S, int64_t s_stride, hipStream_t st);
+                       const int64_t* prior_len, float* S, int64_t s_stride, hipStream_t st,
+                       const int64_t* prior_len_host = nullptr);
 
 // Step 4 for the select API: k_sel[b][g][r] = cache row idx[b][g][r], r < min(budget, T_b).
 hipError_t launch_gather(const SelShape& s, const CacheView& cv, const int64_t* prior_len,

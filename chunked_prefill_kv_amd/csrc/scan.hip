@@ -207,24 +207,55 @@ __global__ __launch_bounds__(256, kScanOcc) void scan_mfma_kernel(const uint16_t
 // With a single query per head (decode, or N_q = 1) the G <= 16 query heads of
 // a KV head form the 16 rows of one MFMA tile; keys stream through registers
 // straight from HBM (this scan is bandwidth-bound: 4 useful rows per key).
+// The workgroups with keys to score, listed by sequence: sequence b owns
+// workgroups [first[b], first[b+1]), h_kv x its key tiles, in (KV head, tile)
+// order; len[b] is its prior length.
+constexpr int kMapSeqs = 256;
+struct TileMap {
+    int32_t n;                          // sequences listed; 0: the grid is batch x h_kv x tiles
+    int32_t first[kMapSeqs + 1];
+    int32_t len[kMapSeqs];
+};
+
 template <int D, int GROUPS>
 __global__ __launch_bounds__(256) void scan_rows16_kernel(const uint16_t* __restrict__ qsel,
                                                          const float* __restrict__ rq, CacheView cv,
                                                          const int64_t* __restrict__ prior_len, int64_t budget,
                                                          int h_kv, int G, int tiles, float* __restrict__ S,
-                                                         int64_t s_stride) {
+                                                         int64_t s_stride, TileMap map) {
     constexpr int KS = D / 32;          // k-steps of 32
     constexpr int KEYS = 4 * GROUPS * 16;
     // slots follow the launch order, so every XCD receives an even share of
     // the key tiles whatever the sequence lengths (grouping a sequence's tiles
     // on one XCD, as the prefill scan does for L2 reuse, buys nothing here:
     // every key is read once)
-    const int bg = blockIdx.x / tiles, tile = blockIdx.x % tiles;
-    const int b = bg / h_kv, g = bg % h_kv;
-    const int64_t T = prior_len[b];
-    if (T <= budget) return;
+    int b, g, tile;
+    int64_t T;
+    if (map.n > 0) {                    // only workgroups with keys were launched
+        const int slot = blockIdx.x;
+        int lo = 0, hi = map.n;         // the largest b with first[b] <= slot (first[n] > slot)
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (map.first[mid] <= slot) lo = mid;
+            else hi = mid;
+        }
+        b = lo;
+        const int per = (map.first[b + 1] - map.first[b]) / h_kv;
+        const int r = slot - map.first[b];
+        g = r / per;
+        tile = r % per;
+        T = map.len[b];
+    } else {
+        const int bg0 = blockIdx.x / tiles;
+        tile = blockIdx.x % tiles;
+        b = bg0 / h_kv;
+        g = bg0 % h_kv;
+        T = prior_len[b];
+        if (T <= budget) return;
+        if (static_cast<int64_t>(tile) * KEYS >= T) return;
+    }
+    const int bg = b * h_kv + g;
     const int64_t key0 = static_cast<int64_t>(tile) * KEYS;
-    if (key0 >= T) return;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int quad = lane >> 4, col = lane & 15;
 
@@ -352,14 +383,35 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const float* __restrict_
 // ----------------------------------------------------------------------------- launcher
 
 hipError_t launch_scan(const SelShape& s, const void* qsel, const float* rq, const CacheView& cv,
-                       const int64_t* prior_len, float* S, int64_t s_stride, hipStream_t st) {
+                       const int64_t* prior_len, float* S, int64_t s_stride, hipStream_t st,
+                       const int64_t* prior_len_host) {
     const int bgs = s.batch * s.h_kv;
     if (s.esz == 2 && s.nq_pad == 1 && !s.qsplit) {   // one query per head, G <= 16
         constexpr int GR = kRows16Groups;
-        const int tiles = static_cast<int>((s.t_max + 64 * GR - 1) / (64 * GR));
+        constexpr int KEYS = 64 * GR;
+        const int tiles = static_cast<int>((s.t_max + KEYS - 1) / KEYS);
         dim3 grid(bgs * tiles), block(256);
-        if (s.d == 128) hipLaunchKernelGGL((scan_rows16_kernel<128, GR>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride);
-        else hipLaunchKernelGGL((scan_rows16_kernel<64, GR>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride);
+        // With the lengths on the host, list only the workgroups that have keys
+        // (a ragged batch otherwise launches batch x h_kv x the longest
+        // sequence's tiles, most of them empty).
+        TileMap map{};
+        if (prior_len_host && s.batch <= kMapSeqs) {
+            int64_t acc = 0;
+            for (int i = 0; i < s.batch; ++i) {
+                const int64_t T = prior_len_host[i];
+                map.first[i] = static_cast<int32_t>(acc);
+                map.len[i] = static_cast<int32_t>(T);
+                acc += T > s.budget ? (T + KEYS - 1) / KEYS * s.h_kv : 0;
+            }
+            map.first[s.batch] = static_cast<int32_t>(acc);
+            if (acc == 0) return hipSuccess;                // nothing to score
+            if (acc <= int64_t(grid.x)) {
+                map.n = s.batch;
+                grid = dim3(static_cast<unsigned>(acc));
+            }
+        }
+        if (s.d == 128) hipLaunchKernelGGL((scan_rows16_kernel<128, GR>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride, map);
+        else hipLaunchKernelGGL((scan_rows16_kernel<64, GR>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride, map);
     } else if (s.esz == 2) {
         // 32-key blocks per wave: 2 for [hi | lo] query pairs (twice the query
         // fragments per key block); for bf16 rows 3 or 2, whichever gives the
