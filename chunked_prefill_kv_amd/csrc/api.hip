@@ -349,7 +349,7 @@ kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, 
     float* comb = scores ? scores : S;
     KVSEL_TRY(traced(KVSEL_K_TOPB, st, [&] { return launch_topb(s.batch * s.h_kv, s.h_kv, S, sc.nsplit, split_stride, comb, s.t_max, T,
                                                                 s.budget, s.t_max, any, at<uint32_t>(ws, L.topb), idx, st,
-                                                                rowidx ? &cv : nullptr, rowidx); }), "key top-B");
+                                                                rowidx ? &cv : nullptr, rowidx, b->prior_len_host); }), "key top-B");
     return KVSEL_OK;
 }
 

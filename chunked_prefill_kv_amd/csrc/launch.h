@@ -69,6 +69,50 @@ hipError_t launch_topk(int problems, int heads_per_seq, const float* scores, int
 // Compute units of the current device (queried once per device; 256 if the
 // query fails).  Launch shapes that run in rounds are sized with it.
 int device_cus();
+
+// A ragged batch's workgroups listed per sequence in the launch arguments
+// (built on the host from the prior lengths), so that a grid holds only the
+// workgroups with work: sequence b owns workgroups [first[b], first[b+1]),
+// heads x its per-head count, in (head, item) order; len[b] is its prior
+// length.  n == 0: no list, the grid spans every sequence up to the longest.
+constexpr int kMapSeqs = 256;
+struct TileMap {
+    int32_t n;
+    int32_t first[kMapSeqs + 1];
+    int32_t len[kMapSeqs];
+};
+// Fill m for per-sequence item counts count(T_b) (times heads); false (m.n = 0)
+// when the batch is too long to list or the list would not be shorter.
+template <typename F>
+bool build_tile_map(TileMap& m, const int64_t* prior_len_host, int batch, int heads, int64_t full_grid, F count) {
+    m.n = 0;
+    if (!prior_len_host || batch > kMapSeqs) return false;
+    int64_t acc = 0;
+    for (int i = 0; i < batch; ++i) {
+        m.first[i] = static_cast<int32_t>(acc);
+        m.len[i] = static_cast<int32_t>(prior_len_host[i]);
+        acc += count(prior_len_host[i]) * heads;
+    }
+    m.first[batch] = static_cast<int32_t>(acc);
+    if (acc > full_grid) return false;
+    m.n = batch;
+    return true;
+}
+// Workgroup blockIdx.x of a listed grid -> (sequence b, head g, item t).
+__device__ __forceinline__ void tile_map_slot(const TileMap& m, int heads, int& b, int& g, int& t) {
+    const int slot = blockIdx.x;
+    int lo = 0, hi = m.n;               // the largest b with first[b] <= slot (first[n] > slot)
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (m.first[mid] <= slot) lo = mid;
+        else hi = mid;
+    }
+    const int per = (m.first[lo + 1] - m.first[lo]) / heads;
+    const int r = slot - m.first[lo];
+    b = lo;
+    g = r / per;
+    t = r % per;
+}
 // The top-B counts kept keys per 2048-key segment in LDS, for at most
 // kTopbMaxSegments segments: max(T_max, budget) <= 2^21.
 constexpr int kTopbSegKeys = 2048;
@@ -78,7 +122,8 @@ size_t topb_scratch_bytes(int problems, int64_t t_max, int64_t budget);
 hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int nsplit, int64_t split_stride,
                        float* comb, int64_t s_stride, const int64_t* prior_len, int64_t budget, int64_t t_max,
                        bool any_select, uint32_t* scratch, int32_t* out, hipStream_t st,
-                       const CacheView* cv = nullptr, int32_t* rowidx = nullptr);
+                       const CacheView* cv = nullptr, int32_t* rowidx = nullptr,
+                       const int64_t* prior_len_host = nullptr);
 
 // Gather the kept query rows of every head into Q_sel[b][g][hh*nq_pad + r][d]
 // (raw rows) and rq = 1/|q|; rows r >= nqp repeat row 0 of that head.  With

@@ -207,16 +207,6 @@ __global__ __launch_bounds__(256, kScanOcc) void scan_mfma_kernel(const uint16_t
 // With a single query per head (decode, or N_q = 1) the G <= 16 query heads of
 // a KV head form the 16 rows of one MFMA tile; keys stream through registers
 // straight from HBM (this scan is bandwidth-bound: 4 useful rows per key).
-// The workgroups with keys to score, listed by sequence: sequence b owns
-// workgroups [first[b], first[b+1]), h_kv x its key tiles, in (KV head, tile)
-// order; len[b] is its prior length.
-constexpr int kMapSeqs = 256;
-struct TileMap {
-    int32_t n;                          // sequences listed; 0: the grid is batch x h_kv x tiles
-    int32_t first[kMapSeqs + 1];
-    int32_t len[kMapSeqs];
-};
-
 template <int D, int GROUPS>
 __global__ __launch_bounds__(256) void scan_rows16_kernel(const uint16_t* __restrict__ qsel,
                                                          const float* __restrict__ rq, CacheView cv,
@@ -232,18 +222,7 @@ __global__ __launch_bounds__(256) void scan_rows16_kernel(const uint16_t* __rest
     int b, g, tile;
     int64_t T;
     if (map.n > 0) {                    // only workgroups with keys were launched
-        const int slot = blockIdx.x;
-        int lo = 0, hi = map.n;         // the largest b with first[b] <= slot (first[n] > slot)
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (map.first[mid] <= slot) lo = mid;
-            else hi = mid;
-        }
-        b = lo;
-        const int per = (map.first[b + 1] - map.first[b]) / h_kv;
-        const int r = slot - map.first[b];
-        g = r / per;
-        tile = r % per;
+        tile_map_slot(map, h_kv, b, g, tile);
         T = map.len[b];
     } else {
         const int bg0 = blockIdx.x / tiles;
@@ -394,21 +373,11 @@ hipError_t launch_scan(const SelShape& s, const void* qsel, const float* rq, con
         // With the lengths on the host, list only the workgroups that have keys
         // (a ragged batch otherwise launches batch x h_kv x the longest
         // sequence's tiles, most of them empty).
-        TileMap map{};
-        if (prior_len_host && s.batch <= kMapSeqs) {
-            int64_t acc = 0;
-            for (int i = 0; i < s.batch; ++i) {
-                const int64_t T = prior_len_host[i];
-                map.first[i] = static_cast<int32_t>(acc);
-                map.len[i] = static_cast<int32_t>(T);
-                acc += T > s.budget ? (T + KEYS - 1) / KEYS * s.h_kv : 0;
-            }
-            map.first[s.batch] = static_cast<int32_t>(acc);
-            if (acc == 0) return hipSuccess;                // nothing to score
-            if (acc <= int64_t(grid.x)) {
-                map.n = s.batch;
-                grid = dim3(static_cast<unsigned>(acc));
-            }
+        TileMap map;
+        if (build_tile_map(map, prior_len_host, s.batch, s.h_kv, grid.x,
+                           [&](int64_t T) -> int64_t { return T > s.budget ? (T + KEYS - 1) / KEYS : 0; })) {
+            if (map.first[s.batch] == 0) return hipSuccess;   // nothing to score
+            grid = dim3(static_cast<unsigned>(map.first[s.batch]));
         }
         if (s.d == 128) hipLaunchKernelGGL((scan_rows16_kernel<128, GR>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride, map);
         else hipLaunchKernelGGL((scan_rows16_kernel<64, GR>), grid, block, 0, st, (const uint16_t*)qsel, rq, cv, prior_len, s.budget, s.h_kv, s.G, tiles, S, s_stride, map);

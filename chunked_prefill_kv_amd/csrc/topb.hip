@@ -49,8 +49,22 @@ struct TopbArgs {
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void topb_hist_kernel(TopbArgs a) {
-    const int p = blockIdx.x / a.nseg, seg = blockIdx.x % a.nseg;
+// Workgroup -> (problem, segment): through the per-sequence list, or the full
+// problems x segments grid.
+__device__ __forceinline__ void segment_of(const TopbArgs& a, const TileMap& m, int& p, int& seg) {
+    if (m.n > 0) {
+        int b, g;
+        tile_map_slot(m, a.heads_per_seq, b, g, seg);
+        p = b * a.heads_per_seq + g;
+    } else {
+        p = blockIdx.x / a.nseg;
+        seg = blockIdx.x % a.nseg;
+    }
+}
+
+__global__ __launch_bounds__(256) void topb_hist_kernel(TopbArgs a, TileMap m) {
+    int p, seg;
+    segment_of(a, m, p, seg);
     const int j0 = seg * kSeg;
     // the first split's scores are requested before the prior length is known
     // (inside the problem's row of s_stride entries; keys past T are dropped)
@@ -268,8 +282,9 @@ __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
     }
 }
 
-__global__ __launch_bounds__(256) void topb_write_kernel(TopbArgs a) {
-    const int p = blockIdx.x / a.nseg, seg = blockIdx.x % a.nseg;
+__global__ __launch_bounds__(256) void topb_write_kernel(TopbArgs a, TileMap m) {
+    int p, seg;
+    segment_of(a, m, p, seg);
     // wave w owns keys [j0 + 512 w, j0 + 512 (w + 1)) in 8 steps of 64; the
     // scores are requested first, before the prior length, the threshold and
     // the earlier segments' counts (inside the problem's row of s_stride
@@ -358,7 +373,7 @@ size_t topb_scratch_bytes(int problems, int64_t t_max, int64_t budget) {
 hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int nsplit, int64_t split_stride,
                        float* comb, int64_t s_stride, const int64_t* prior_len, int64_t budget, int64_t t_max,
                        bool any_select, uint32_t* scratch, int32_t* out, hipStream_t st, const CacheView* cv,
-                       int32_t* rowidx) {
+                       int32_t* rowidx, const int64_t* prior_len_host) {
     TopbArgs a;
     a.cv = cv ? *cv : CacheView{};
     a.rowidx = cv ? rowidx : nullptr;
@@ -376,12 +391,23 @@ hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int n
     a.segc = a.thr + size_t(problems) * 2;
     a.out = out;
     if (a.nseg > kTopbMaxSegments) return hipErrorInvalidValue;   // rejected on the host before any launch
-    const dim3 grid_seg(problems * a.nseg);
-    if (any_select) {
-        hipLaunchKernelGGL(topb_hist_kernel, grid_seg, dim3(256), 0, st, a);
+    // with the prior lengths on the host, only the segments with keys (the
+    // histogram: of selecting sequences; the write: up to max(T_b, budget))
+    const int64_t full = int64_t(problems) * a.nseg;
+    const int batch = problems / heads_per_seq;
+    TileMap mh, mw;
+    dim3 grid_h(static_cast<unsigned>(full)), grid_w(static_cast<unsigned>(full));
+    if (build_tile_map(mh, prior_len_host, batch, heads_per_seq, full,
+                       [&](int64_t T) -> int64_t { return T > budget ? (T + kSeg - 1) / kSeg : 0; }))
+        grid_h = dim3(static_cast<unsigned>(mh.first[batch]));
+    if (build_tile_map(mw, prior_len_host, batch, heads_per_seq, full,
+                       [&](int64_t T) -> int64_t { return ((T > budget ? T : budget) + kSeg - 1) / kSeg; }))
+        grid_w = dim3(static_cast<unsigned>(mw.first[batch]));
+    if (any_select && grid_h.x > 0) {
+        hipLaunchKernelGGL(topb_hist_kernel, grid_h, dim3(256), 0, st, a, mh);
         hipLaunchKernelGGL(topb_thresh_kernel, dim3(problems), dim3(1024), 0, st, a);
     }
-    hipLaunchKernelGGL(topb_write_kernel, grid_seg, dim3(256), 0, st, a);
+    if (grid_w.x > 0) hipLaunchKernelGGL(topb_write_kernel, grid_w, dim3(256), 0, st, a, mw);
     return hipGetLastError();
 }
 

@@ -245,18 +245,21 @@ def test_decode_group_pooling_single_token():
             parity.check_idx(S_or[g], wl.B, idx_h[b, g], S_h[b, g, :T])
 
 
-@pytest.mark.parametrize("variant", ["gqa", "mqa_g32", "gqa_block8", "gqa_block24", "g16_d64"])
+@pytest.mark.parametrize("variant", ["gqa", "mqa_g32", "gqa_block8", "gqa_block24", "g16_d64", "many_seqs"])
 def test_decode_paged_matches_oracle(variant):
     """Ragged batch, chunk of 1, paged cache with a shuffled block table; some
     sequences are shorter than the budget (no selection).  Blocks of 8 and 24
     rows put a block boundary inside a 16-key group of the one-query scan; 16
-    heads per KV head fill its MFMA rows, with d = 64."""
+    heads per KV head fill its MFMA rows, with d = 64.  300 sequences are more
+    than the one-query scan lists in its launch arguments (its grid then spans
+    every sequence's tiles up to the longest)."""
     base = gen.WORKLOADS["decode_paged"]
     wl = {"gqa": base.replace(batch=6, decode_len_lo=300, decode_len_hi=2500, B=512),
           "mqa_g32": base.replace(batch=3, decode_len_lo=700, decode_len_hi=1800, H_q=32, H_kv=1, B=400),
           "gqa_block8": base.replace(batch=4, decode_len_lo=300, decode_len_hi=2100, B=512, block_size=8),
           "gqa_block24": base.replace(batch=4, decode_len_lo=300, decode_len_hi=2100, B=512, block_size=24),
-          "g16_d64": base.replace(batch=4, decode_len_lo=300, decode_len_hi=2100, B=512, H_q=32, H_kv=2, d=64)}[variant]
+          "g16_d64": base.replace(batch=4, decode_len_lo=300, decode_len_hi=2100, B=512, H_q=32, H_kv=2, d=64),
+          "many_seqs": base.replace(batch=300, decode_len_lo=60, decode_len_hi=700, B=128, H_q=8, H_kv=2)}[variant]
     print(f"[case] decode {variant}", flush=True)
     di = gen.decode_inputs(wl)
     dr = runner.DecodeRunner(wl, di, out_dtype=torch.float32)
