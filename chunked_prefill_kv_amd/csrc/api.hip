@@ -96,11 +96,16 @@ hipError_t traced(int id, hipStream_t st, F&& fn) {
         if (g_trace.mask & (1u << id)) {
             a = g_trace.take();
             b = g_trace.take();
+            if (!a || !b) {                    // an event could not be created: this launch is not timed
+                if (a) g_trace.pool.push_back(a);
+                if (b) g_trace.pool.push_back(b);
+                a = b = nullptr;
+            }
         }
     }
     if (a) (void)hipEventRecord(a, st);
     const hipError_t e = fn();
-    if (a && b) {
+    if (a) {
         (void)hipEventRecord(b, st);
         std::lock_guard<std::mutex> lk(g_trace.mu);
         g_trace.recs.push_back({id, a, b});

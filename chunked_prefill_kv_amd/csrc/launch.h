@@ -94,7 +94,7 @@ bool build_tile_map(TileMap& m, const int64_t* prior_len_host, int batch, int he
         acc += count(prior_len_host[i]) * heads;
     }
     m.first[batch] = static_cast<int32_t>(acc);
-    if (acc > full_grid) return false;
+    if (acc > full_grid || acc > INT32_MAX) return false;
     m.n = batch;
     return true;
 }
