@@ -120,6 +120,12 @@ __device__ __forceinline__ uint32_t excl_scan_1024(uint32_t v, uint32_t* wsum) {
     return off + incl - v;
 }
 
+// FUSED (problems of at most kFusedKeys keys): the workgroup also sums the
+// scan's split partials and counts the histogram itself, with every score of
+// the problem held in registers (no histogram launch, one read of the scores).
+constexpr int kFusedSteps = 4;                  // 8192-key steps held in registers
+constexpr int kFusedKeys = kFusedSteps * 8192;
+template <bool FUSED>
 __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
     const int p = blockIdx.x;
     const int64_t T64 = a.prior_len[p / a.heads_per_seq];
@@ -145,12 +151,56 @@ __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
             v[i] = c[j < T ? j : T - 1];
         }
     };
-    load_step(0);
-    const uint32_t* h = a.hist + static_cast<int64_t>(p) * kBins;
-    for (int i = tid; i < kBins; i += 1024) hs[i] = h[i];
+    constexpr int NST = FUSED ? kFusedSteps : 1;
+    float vs[NST][8];                              // FUSED: key base0 + 512 wave + 64 i + lane, base0 = 8192 st
+    if constexpr (FUSED) {
+        // the scan's partials added in split order (as the histogram launch
+        // does), the sum kept in registers and stored as the score
+        const float* x = a.part + static_cast<int64_t>(p) * a.s_stride;
+        float* cw = a.comb + static_cast<int64_t>(p) * a.s_stride;
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int j = st * 8192 + wave * 512 + i * kWave + lane;
+                vs[st][i] = x[j < T ? j : T - 1];
+            }
+        for (int sp = 1; sp < a.nsplit; ++sp)
+#pragma unroll
+            for (int st = 0; st < NST; ++st)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int j = st * 8192 + wave * 512 + i * kWave + lane;
+                    if (j < T) vs[st][i] += x[sp * a.split_stride + j];
+                }
+        if (a.nsplit > 1 || cw != x) {
+#pragma unroll
+            for (int st = 0; st < NST; ++st)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int j = st * 8192 + wave * 512 + i * kWave + lane;
+                    if (j < T) cw[j] = vs[st][i];
+                }
+        }
+        for (int i = tid; i < kBins; i += 1024) hs[i] = 0;
+    } else {
+        load_step(0);
+        const uint32_t* h = a.hist + static_cast<int64_t>(p) * kBins;
+        for (int i = tid; i < kBins; i += 1024) hs[i] = h[i];
+    }
     for (int i = tid; i < a.nseg; i += 1024) { sgt[i] = 0; seq_[i] = 0; }
     if (tid == 0) { s_cnt = 0; s_bin = 0; s_need = 1; s_digit = 0; s_rem = 1; }
     __syncthreads();
+    if constexpr (FUSED) {
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int j = st * 8192 + wave * 512 + i * kWave + lane;
+                if (j < T) atomicAdd(&hs[value_bin(vs[st][i])], 1u);
+            }
+        __syncthreads();
+    }
     // boundary bin: thread t owns bins 4(1023-t) .. +3, scanned from the top
     {
         const int t = 1023 - tid;
@@ -173,12 +223,20 @@ __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
     // 64 (one segment: the count stays in a register, one LDS atomic per wave
     // and pass), boundary keys are appended with one atomic per wave and step.
     const uint64_t lt = (1ull << lane) - 1ull;
-    for (int base0 = 0; base0 < T; base0 += 8 * 1024) {
+#pragma unroll
+    for (int st = 0; st < (FUSED ? NST : 1 << 20); ++st) {
+        const int base0 = st * 8 * 1024;
+        if (base0 >= T) break;
         const int wbase = base0 + wave * 512;
         float cur[8];
+        if constexpr (FUSED) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) cur[i] = v[i];
-        if (base0 + 8 * 1024 < T) load_step(base0 + 8 * 1024);
+            for (int i = 0; i < 8; ++i) cur[i] = vs[st < NST ? st : 0][i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) cur[i] = v[i];
+            if (base0 + 8 * 1024 < T) load_step(base0 + 8 * 1024);
+        }
         uint32_t ngt = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -391,6 +449,10 @@ hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int n
     a.segc = a.thr + size_t(problems) * 2;
     a.out = out;
     if (a.nseg > kTopbMaxSegments) return hipErrorInvalidValue;   // rejected on the host before any launch
+    // few problems of at most kFusedKeys keys: one fused threshold launch
+    // (sums, histogram and threshold from registers) in place of two
+    // (and at most two split partials: the workgroup adds them alone)
+    const bool fused = problems <= 64 && t_max <= kFusedKeys && nsplit <= 2;
     // with the prior lengths on the host, only the segments with keys (the
     // histogram: of selecting sequences; the write: up to max(T_b, budget))
     const int64_t full = int64_t(problems) * a.nseg;
@@ -404,8 +466,12 @@ hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int n
                        [&](int64_t T) -> int64_t { return ((T > budget ? T : budget) + kSeg - 1) / kSeg; }))
         grid_w = dim3(static_cast<unsigned>(mw.first[batch]));
     if (any_select && grid_h.x > 0) {
-        hipLaunchKernelGGL(topb_hist_kernel, grid_h, dim3(256), 0, st, a, mh);
-        hipLaunchKernelGGL(topb_thresh_kernel, dim3(problems), dim3(1024), 0, st, a);
+        if (fused) {
+            hipLaunchKernelGGL(topb_thresh_kernel<true>, dim3(problems), dim3(1024), 0, st, a);
+        } else {
+            hipLaunchKernelGGL(topb_hist_kernel, grid_h, dim3(256), 0, st, a, mh);
+            hipLaunchKernelGGL(topb_thresh_kernel<false>, dim3(problems), dim3(1024), 0, st, a);
+        }
     }
     if (grid_w.x > 0) hipLaunchKernelGGL(topb_write_kernel, grid_w, dim3(256), 0, st, a, mw);
     return hipGetLastError();
