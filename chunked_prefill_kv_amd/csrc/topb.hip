@@ -13,6 +13,9 @@
 //                and the number of keys equal to tau that are kept, and per
 //                segment the number of kept keys above / equal to tau;
 //   topb_write   (problem x segment)  ordered write of the kept indices.
+// For few short problems topb_thresh also does topb_hist's work (its
+// workgroup holds the problem's scores in registers).  With the prior lengths
+// on the host, the segment grids list only the segments that have keys.
 #include "launch.h"
 
 namespace kvsel {
