@@ -115,7 +115,8 @@ typedef struct {
 #define KVSEL_MAX_SELECT_KEYS (2048 * 1024)
 
 /* Workspace bytes that kvsel_select and kvsel_prefill_chunk need for these
- * shapes (the larger of the two).  Writes *bytes; returns a status (so that
+ * shapes (the larger of the two) on the current device (some launch shapes
+ * follow its compute-unit count).  Writes *bytes; returns a status (so that
  * an invalid or unsupported shape is reported, not sized). */
 kvsel_status kvsel_workspace_size(const kvsel_heads *heads, const kvsel_batch *batch,
                                   const kvsel_params *params, size_t *bytes);
