@@ -24,7 +24,10 @@
  *     device memory, including the workspace; the library allocates nothing
  *     and keeps no per-call state.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
- *     enqueues work on it and returns without synchronising.
+ *     enqueues kernel launches on it (no memset, copy or host wait) and
+ *     returns without synchronising, so calls can be captured in a HIP graph
+ *     while kernel tracing is off; a replay reads the argument values of the
+ *     captured calls, so their buffers must stay allocated.
  *   - Arguments are checked on the host before anything is enqueued; on an
  *     error the call returns a non-zero kvsel_status with nothing enqueued and
  *     kvsel_last_error() describes it.  A failed launch returns
