@@ -333,7 +333,7 @@ kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, 
         SelShape sq = sc;
         sq.esz = 4;                                          // qbar is fp32
         KVSEL_TRY(traced(KVSEL_K_QPOOL, st, [&] { return launch_qpool(s, q, T, qbar, st); }), "query pooling");
-        KVSEL_TRY(traced(KVSEL_K_QSTATS, st, [&] { return launch_qstats(sq, qbar, T, at<double>(ws, L.qpart), at<float>(ws, L.qcos), at<float>(ws, L.qrn), at<uint32_t>(ws, L.topb), int64_t(s.batch) * s.h_kv * 4096, st); }), "query statistics");
+        KVSEL_TRY(traced(KVSEL_K_QSTATS, st, [&] { return launch_qstats(sq, qbar, T, at<double>(ws, L.qpart), at<float>(ws, L.qcos), at<float>(ws, L.qrn), at<uint32_t>(ws, L.topb), int64_t(topb_zero_words(s.batch * s.h_kv)), st); }), "query statistics");
         KVSEL_TRY(traced(KVSEL_K_QTOPK, st, [&] { return launch_topk(s.batch * s.h_kv, s.h_kv, at<float>(ws, L.qcos), s.C, 1, 0, nullptr, T, s.C, s.budget, s.nqp, keep, s.nqp,
                               1, s.C, st); }), "query top-k");
         KVSEL_TRY(traced(KVSEL_K_QPACK, st, [&] { return launch_pack_pooled(sc, qbar, keep, s.nqp, T, at<void>(ws, L.qsel), at<float>(ws, L.rq), st); }), "query packing");
@@ -342,12 +342,12 @@ kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, 
         int32_t* keep = q_keep ? q_keep : at<int32_t>(ws, L.keep);
         const bool keep_all = s.nqp == s.C;   // every query kept: no statistics to take (decode)
         if (!keep_all) {
-            KVSEL_TRY(traced(KVSEL_K_QSTATS, st, [&] { return launch_qstats(s, q, T, at<double>(ws, L.qpart), at<float>(ws, L.qcos), at<float>(ws, L.qrn), at<uint32_t>(ws, L.topb), int64_t(s.batch) * s.h_kv * 4096, st); }), "query statistics");
+            KVSEL_TRY(traced(KVSEL_K_QSTATS, st, [&] { return launch_qstats(s, q, T, at<double>(ws, L.qpart), at<float>(ws, L.qcos), at<float>(ws, L.qrn), at<uint32_t>(ws, L.topb), int64_t(topb_zero_words(s.batch * s.h_kv)), st); }), "query statistics");
             KVSEL_TRY(traced(KVSEL_K_QTOPK, st, [&] { return launch_topk(s.batch * s.h_q, s.h_q, at<float>(ws, L.qcos), s.C, 1, 0, nullptr, T, s.C, s.budget, s.nqp, keep, s.nqp,
                                   1, s.C, st); }), "query top-k");
         }
         KVSEL_TRY(traced(KVSEL_K_QPACK, st, [&] { return launch_pack_qsel(s, q, keep, s.nqp, at<float>(ws, L.qrn), T, at<void>(ws, L.qsel), at<float>(ws, L.rq), st,
-                                                                         keep_all, at<uint32_t>(ws, L.topb), int64_t(s.batch) * s.h_kv * 4096); }),
+                                                                         keep_all, at<uint32_t>(ws, L.topb), int64_t(topb_zero_words(s.batch * s.h_kv))); }),
                   "query packing");
         KVSEL_TRY(traced(KVSEL_K_SCAN, st, [&] { return launch_scan(s, at<void>(ws, L.qsel), at<float>(ws, L.rq), cv, T, S, s.t_max, st, b->prior_len_host); }), "key scan");
     }

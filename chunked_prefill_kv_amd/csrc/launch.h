@@ -63,9 +63,9 @@ hipError_t launch_topk(int problems, int heads_per_seq, const float* scores, int
 // writes out[p][0..budget) (kept indices ascending, -1 past T_p) for every
 // problem p = b * heads_per_seq + g, and with cv / rowidx given the cache row
 // number of every kept position (rowidx[p][r], for the gathering attention).  comb receives the summed scores (may be
-// `part` itself).  scratch: topb_scratch_bytes(); its histogram part
-// (problems * 4096 uint32 at its start) must be zero on entry when
-// any_select (launch_qstats clears it).
+// `part` itself).  scratch: topb_scratch_bytes(); its first
+// topb_zero_words(problems) words (the histogram) must be zero on entry when
+// any_select (launch_qstats or launch_pack_qsel clears them).
 // Compute units of the current device (queried once per device; 256 if the
 // query fails).  Launch shapes that run in rounds are sized with it.
 int device_cus();
@@ -119,6 +119,8 @@ constexpr int kTopbSegKeys = 2048;
 constexpr int kTopbMaxSegments = 1024;
 int topb_segments(int64_t t_max, int64_t budget);
 size_t topb_scratch_bytes(int problems, int64_t t_max, int64_t budget);
+// Words at the start of the top-B scratch that must be zero on entry.
+size_t topb_zero_words(int problems);
 hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int nsplit, int64_t split_stride,
                        float* comb, int64_t s_stride, const int64_t* prior_len, int64_t budget, int64_t t_max,
                        bool any_select, uint32_t* scratch, int32_t* out, hipStream_t st,

@@ -65,6 +65,9 @@ __device__ __forceinline__ void segment_of(const TopbArgs& a, const TileMap& m, 
     }
 }
 
+// SPLIT: the scan left more than one split partial (the one-split form keeps
+// no registers for the other splits' loads).
+template <bool SPLIT>
 __global__ __launch_bounds__(256) void topb_hist_kernel(TopbArgs a, TileMap m) {
     int p, seg;
     segment_of(a, m, p, seg);
@@ -84,12 +87,23 @@ __global__ __launch_bounds__(256) void topb_hist_kernel(TopbArgs a, TileMap m) {
     __shared__ uint32_t lh[kBins];
     for (int i = threadIdx.x; i < kBins; i += 256) lh[i] = 0;
     __syncthreads();
-    for (int sp = 1; sp < a.nsplit; ++sp) {          // partials added in split order
+    // the other splits' partials, four splits' loads in flight at a time,
+    // added in split order
+    if (SPLIT)
+    for (int sp0 = 1; sp0 < a.nsplit; sp0 += 4) {
+        float w[4][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int j = j0 + i * 256 + threadIdx.x;
-            if (j < T) v[i] += x[sp * a.split_stride + j];
-        }
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int j = j0 + i * 256 + threadIdx.x;
+                w[q][i] = (sp0 + q < a.nsplit && j < T) ? x[(sp0 + q) * a.split_stride + j] : 0.0f;
+            }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (sp0 + q < a.nsplit) v[i] += w[q][i];
     }
     float* c = a.comb + static_cast<int64_t>(p) * a.s_stride;
 #pragma unroll
@@ -128,8 +142,9 @@ __device__ __forceinline__ uint32_t excl_scan_1024(uint32_t v, uint32_t* wsum) {
 // the problem held in registers (no histogram launch, one read of the scores).
 constexpr int kFusedSteps = 4;                  // 8192-key steps held in registers
 constexpr int kFusedKeys = kFusedSteps * 8192;
-template <bool FUSED>
+template <bool FUSED, int NST>
 __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
+    static_assert(!FUSED || NST == kFusedSteps, "the fused form holds every step");
     const int p = blockIdx.x;
     const int64_t T64 = a.prior_len[p / a.heads_per_seq];
     if (T64 <= a.budget) return;
@@ -142,20 +157,19 @@ __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
     __shared__ uint32_t wsum[16];
     __shared__ uint32_t s_bin, s_need, s_cnt, s_digit, s_rem, s_full;
     const float* c = a.comb + static_cast<int64_t>(p) * a.s_stride;
-    // the pass's first scores are requested before the histogram, so they
-    // arrive while the boundary bin is found; each later step's scores are
-    // requested one step ahead (wave w reads [base0 + 512 w, +512) in 8
-    // loads of 64)
-    float v[8];
-    auto load_step = [&](int base0) {
+    // The scores pass over the keys in 8192-key steps (wave w takes
+    // [base0 + 512 w, +512) in 8 loads of 64), held in a ring of NST steps of
+    // registers: FUSED holds every step; otherwise the first NST steps are
+    // requested before the histogram (they arrive while the boundary bin is
+    // found) and each later step NST steps ahead.
+    float vs[NST][8];                              // key 8192 st + 512 wave + 64 i + lane
+    auto load_step = [&](int st, float (&dst)[8]) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int j = base0 + wave * 512 + i * kWave + lane;
-            v[i] = c[j < T ? j : T - 1];
+            const int j = st * 8192 + wave * 512 + i * kWave + lane;
+            dst[i] = c[j < T ? j : T - 1];
         }
     };
-    constexpr int NST = FUSED ? kFusedSteps : 1;
-    float vs[NST][8];                              // FUSED: key base0 + 512 wave + 64 i + lane, base0 = 8192 st
     if constexpr (FUSED) {
         // the scan's partials added in split order (as the histogram launch
         // does), the sum kept in registers and stored as the score
@@ -187,7 +201,9 @@ __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
         }
         for (int i = tid; i < kBins; i += 1024) hs[i] = 0;
     } else {
-        load_step(0);
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+            if (st * 8192 < T) load_step(st, vs[st]);
         const uint32_t* h = a.hist + static_cast<int64_t>(p) * kBins;
         for (int i = tid; i < kBins; i += 1024) hs[i] = h[i];
     }
@@ -226,20 +242,17 @@ __global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
     // 64 (one segment: the count stays in a register, one LDS atomic per wave
     // and pass), boundary keys are appended with one atomic per wave and step.
     const uint64_t lt = (1ull << lane) - 1ull;
+    for (int st0 = 0; st0 * 8192 < T; st0 += NST)
 #pragma unroll
-    for (int st = 0; st < (FUSED ? NST : 1 << 20); ++st) {
-        const int base0 = st * 8 * 1024;
+    for (int r = 0; r < NST; ++r) {
+        const int st = st0 + r;
+        const int base0 = st * 8192;
         if (base0 >= T) break;
         const int wbase = base0 + wave * 512;
         float cur[8];
-        if constexpr (FUSED) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) cur[i] = vs[st < NST ? st : 0][i];
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) cur[i] = v[i];
-            if (base0 + 8 * 1024 < T) load_step(base0 + 8 * 1024);
-        }
+        for (int i = 0; i < 8; ++i) cur[i] = vs[r][i];
+        if (!FUSED && (st + NST) * 8192 < T) load_step(st + NST, vs[r]);
         uint32_t ngt = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -426,6 +439,8 @@ int topb_segments(int64_t t_max, int64_t budget) {
     return static_cast<int>((n + kSeg - 1) / kSeg);
 }
 
+size_t topb_zero_words(int problems) { return size_t(problems) * kBins; }
+
 size_t topb_scratch_bytes(int problems, int64_t t_max, int64_t budget) {
     const int nseg = topb_segments(t_max, budget);
     return size_t(problems) * (kBins + 2 + 2 * size_t(nseg)) * 4;
@@ -470,10 +485,18 @@ hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int n
         grid_w = dim3(static_cast<unsigned>(mw.first[batch]));
     if (any_select && grid_h.x > 0) {
         if (fused) {
-            hipLaunchKernelGGL(topb_thresh_kernel<true>, dim3(problems), dim3(1024), 0, st, a);
+            hipLaunchKernelGGL((topb_thresh_kernel<true, kFusedSteps>), dim3(problems), dim3(1024), 0, st, a);
         } else {
-            hipLaunchKernelGGL(topb_hist_kernel, grid_h, dim3(256), 0, st, a, mh);
-            hipLaunchKernelGGL(topb_thresh_kernel<false>, dim3(problems), dim3(1024), 0, st, a);
+            if (nsplit > 1) hipLaunchKernelGGL(topb_hist_kernel<true>, grid_h, dim3(256), 0, st, a, mh);
+            else hipLaunchKernelGGL(topb_hist_kernel<false>, grid_h, dim3(256), 0, st, a, mh);
+            // fewer problems than CUs: each workgroup keeps four steps of
+            // loads in flight (its latency is the launch's); otherwise one
+            // step, and more workgroups share each CU (on the 512-problem
+            // decode batch: 101 us per step against 113 with four)
+            if (problems < device_cus())
+                hipLaunchKernelGGL((topb_thresh_kernel<false, 4>), dim3(problems), dim3(1024), 0, st, a);
+            else
+                hipLaunchKernelGGL((topb_thresh_kernel<false, 1>), dim3(problems), dim3(1024), 0, st, a);
         }
     }
     if (grid_w.x > 0) hipLaunchKernelGGL(topb_write_kernel, grid_w, dim3(256), 0, st, a, mw);

@@ -504,8 +504,8 @@ def test_sparse_attn_empty_set_without_arrays():
         parity.check_close(O[s], ref, parity.o_tol("bf16"), f"O seq {s}")
 
 
-@pytest.mark.parametrize("dup,H_q", [(12000, 4), (9000, 4), (12000, 2)])
-def test_topb_boundary_bin_over_capacity(dup, H_q):
+@pytest.mark.parametrize("dup,H_q,T", [(12000, 4, 20480), (9000, 4, 20480), (12000, 2, 20480), (12000, 4, 40960)])
+def test_topb_boundary_bin_over_capacity(dup, H_q, T):
     """More prior keys than the threshold search keeps on chip (6144) share
     the value bin of the B-th score (an exact-duplicate key row repeated `dup`
     times, plus near-duplicates one
@@ -514,9 +514,11 @@ def test_topb_boundary_bin_over_capacity(dup, H_q):
     kept set must be the exact top-B of the GPU's own scores (ties to the lower
     index) and match the oracle outside the 1e-4 band.  With 2 query heads the
     scan splits the KV head at most twice and the threshold launch also sums
-    the partials and counts the histogram itself (the fused form)."""
-    rng = np.random.default_rng([0x5EED, 4242, dup])
-    H_kv, d, C, T = 1, 128, 64, 20480
+    the partials and counts the histogram itself (the fused form).  With 40960
+    keys the threshold search holds the scores in a ring of four 8192-key
+    steps of registers and reloads it."""
+    rng = np.random.default_rng([0x5EED, 4242, dup] + ([] if T == 20480 else [T]))
+    H_kv, d, C = 1, 128, 64
     base = gen.WORKLOADS["llama8b_32k"]
     wl = base.replace(L=T + C, C=C, H_q=H_q, H_kv=H_kv, n_q=8, B=1)
     q = gen.f32_to_bf16_bits((0.5 * rng.standard_normal((H_q, C, d)) + 1.0).astype(np.float32))
