@@ -32,6 +32,16 @@ __device__ __forceinline__ float half_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Row sum of the softmax weights as rounded for the P.V MFMAs: one v_dot2
+// with (1, 1) per packed bf16 pair (half the adds of summing the fp32 values;
+// the normaliser is then the sum of the weights the products use).  The
+// 4-wave kernel sums this way (1% faster there); the ping-pong kernel adds
+// the fp32 values (1% slower with the pairs).
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float add_pair(uint32_t w, float acc) {
+    const bf16x2v ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w), ones, acc, false);
+}
 __device__ __forceinline__ int sigma(int m) {
     const int a = m >> 3, hb = (m >> 2) & 1, c = m & 3;
     return 16 * (a >> 1) + 8 * hb + 4 * (a & 1) + c;
@@ -267,6 +277,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x16{};
     float m = -INFINITY, l = 0.0f;
+    float l2[2] = {0.0f, 0.0f};                 // row sum in two chains (l: their total at the end)
     const int krow = sigma(col);
     // K fragment of the S MFMA: key 32*kb2 + krow, elements 16*ks + 8*half .. +7
     auto kfrag = [&](int buf, int kb2, int ks) -> bf16x8 {
@@ -321,7 +332,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
             const float m_new = fmaxf(m, mt);
             if (__ballot((m_new - m) * cl2 > 8.0f) != 0ull) {
                 const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m - m_new) * cl2);
-                l *= alpha;
+                l2[0] *= alpha;
+                l2[1] *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -338,8 +350,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
                 for (int e = 0; e < 4; ++e) {
                     const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e], cl2, -mc));
                     const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e + 1], cl2, -mc));
-                    l += p0 + p1;
                     w[e] = pack_bf16x2(p0, p1);
+                    l2[e & 1] = add_pair(w[e], l2[e & 1]);
                 }
                 pf[k16] = __builtin_bit_cast(bf16x8, w);
             }
@@ -424,7 +436,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
     };
     for (int u = 0; u < ntiles; ++u) step(u, u & 1);
 
-    l = half_sum(l);
+    l = half_sum(l2[0] + l2[1]);
     if (!rvalid) return;
     if (ksplit > 1) {                            // partial: O unnormalised, (m, l) per row
         const int64_t rows_total = static_cast<int64_t>(gridDim.x / (row_blocks * ksplit)) * nrows;
