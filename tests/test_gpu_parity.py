@@ -327,6 +327,10 @@ def test_bitwise_deterministic():
     (30, [0, 60, 300], 90),            # gathering attention (G*C = 120)
     (200, [600, 800], 600),            # T = B exactly (everything kept), T = B + one chunk
     (30, [90, 120, 150], 90),          # the same edge with the gathering attention
+    # 8 sequences x 2 KV heads x 32 row blocks of 128 rows: one round of two
+    # 4-wave workgroups per CU on 256 CUs, the heaviest row blocks paired with
+    # the lightest on each CU, prior lists of 0, 1024 and 1500 keys
+    (1024, [0, 1024, 2048, 3072, 2048, 3072, 1024, 3072], 1500),
 ])
 def test_batched_prefill_ragged(C, Ts, B):
     """Several sequences in one kvsel_prefill_chunk call, each with its own
