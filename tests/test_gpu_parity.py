@@ -53,10 +53,11 @@ def _bits(x: np.ndarray) -> np.ndarray:
     return x.view(np.uint32) if x.dtype == np.float32 else x
 
 
-def check_chunk(r: runner.PromptRunner, k: int, chunks, c64, heads=None, pooling="head"):
+def check_chunk(r: runner.PromptRunner, k: int, chunks, c64, heads=None, pooling="head", otol=None):
     """select (with debug outputs) then prefill_chunk for chunk k; every rule on KV heads `heads`.
     pooling="group": the kept tokens are per KV head and are checked on the
-    oracle's pooled rows; the scores against the oracle's group-pooled scan."""
+    oracle's pooled rows; the scores against the oracle's group-pooled scan.
+    otol: the output tolerance (default: that of the input type)."""
     wl = r.wl
     T, C = r.starts[k], r.lens[k]
     Qc, Kc, Vc = c64[k]
@@ -119,7 +120,7 @@ def check_chunk(r: runner.PromptRunner, k: int, chunks, c64, heads=None, pooling
     Og = r.outs[k][0].double().cpu().numpy()
     for g in heads:
         O_or = quoka.attend(Qc[g * G:(g + 1) * G], sel_k[g:g + 1], sel_v[g:g + 1], Kc[g:g + 1], Vc[g:g + 1])
-        parity.check_close(Og[g * G:(g + 1) * G], O_or, parity.o_tol(wl.dtype), f"O chunk {k} head {g}")
+        parity.check_close(Og[g * G:(g + 1) * G], O_or, otol or parity.o_tol(wl.dtype), f"O chunk {k} head {g}")
     return idx_h
 
 
@@ -137,7 +138,8 @@ def test_prefill_matches_oracle(name):
         check_chunk(r, k, chunks, c64)
 
 
-GROUP = ["bf16_gqa_ragged", "bf16_mqa", "f32_d128", "bf16_d64", "bf16_nq1", "bf16_keep_all_queries", "bf16_g1"]
+GROUP = ["bf16_gqa_ragged", "bf16_mqa", "f32_d128", "tiny_f32_full", "bf16_d64", "bf16_nq1", "bf16_keep_all_queries",
+         "bf16_g1"]
 
 
 @pytest.mark.parametrize("name", GROUP)
@@ -157,6 +159,90 @@ def test_group_pooled_prefill_matches_oracle(name):
     r.load(chunks, keep_idx=True)
     for k in range(wl.n_chunks):
         check_chunk(r, k, chunks, c64, pooling="group")
+
+
+# bf16 output: d = 64 packed (key-split merge), in place (chunks with T <= B)
+# and gathering (G*C <= 128) attention; the fp32 attention at d = 128 and 64
+BF16_OUT = {
+    "bf16_d64": SMALL["bf16_d64"],
+    "bf16_d64_short": LLAMA.replace(L=600, C=16, H_q=16, H_kv=2, d=64, n_q=8, B=150),
+    "f32_d128": SMALL["f32_d128"],
+    "tiny_f32_full": TINY,
+}
+
+
+@pytest.mark.parametrize("name", list(BF16_OUT))
+def test_prefill_bf16_output_matches_oracle(name):
+    """Every chunk of the prompt with the output written as bf16: the same
+    rules, the output within 2e-2 (its bf16 rounding included)."""
+    wl = BF16_OUT[name]
+    print(f"[case] prefill, bf16 output, {name} {wl}", flush=True)
+    chunks = [gen.chunk_inputs(wl, k) for k in range(wl.n_chunks)]
+    c64 = _f64(chunks)
+    r = runner.PromptRunner(wl, out_dtype=torch.bfloat16)
+    r.load(chunks, keep_idx=True)
+    for k in range(wl.n_chunks):
+        check_chunk(r, k, chunks, c64, otol=2e-2)
+
+
+# selection only, in launch forms the prompts above do not reach:
+#   statistics in 128-row blocks (at least 1024 workgroups of them);
+#   the d = 64 scan with three and four 32-key blocks per wave (one round of
+#   workgroups with 8 KV heads at T = 20000 and T = 30000);
+#   the query top-k over a chunk longer than its on-chip key store (30720)
+SELECT_FORMS = {
+    "rows128_f32_d128": dict(dtype="f32", H_q=32, H_kv=8, d=128, C=4096, T=600, B=300, n_q=64),
+    "rows128_f32_d64": dict(dtype="f32", H_q=32, H_kv=8, d=64, C=4096, T=600, B=300, n_q=64),
+    "rows128_bf16_d64": dict(dtype="bf16", H_q=32, H_kv=8, d=64, C=4096, T=600, B=300, n_q=64),
+    "scan_d64_nb3": dict(dtype="bf16", H_q=16, H_kv=8, d=64, C=64, T=20000, B=1024, n_q=16),
+    "scan_d64_nb4": dict(dtype="bf16", H_q=16, H_kv=8, d=64, C=64, T=30000, B=1024, n_q=16),
+    "keep_long_chunk": dict(dtype="bf16", H_q=1, H_kv=1, d=64, C=32768, T=200, B=100, n_q=64),
+}
+
+
+@pytest.mark.parametrize("name", list(SELECT_FORMS))
+def test_select_forms_match_oracle(name):
+    """kvsel_select on seeded inputs (queries with a shared direction, so the
+    cosines to the mean spread): kept queries, scores and index sets against
+    the oracle."""
+    cfg = SELECT_FORMS[name]
+    H_q, H_kv, d, C, T, B, n_q = (cfg[x] for x in ("H_q", "H_kv", "d", "C", "T", "B", "n_q"))
+    G = H_q // H_kv
+    print(f"[case] select {name} {cfg}", flush=True)
+    rng = np.random.default_rng([0x5EED, 77, sum(map(ord, name))])
+    shared = rng.standard_normal(d)
+    qf = (0.6 * rng.standard_normal((H_q, C, d)) + shared).astype(np.float32)
+    kf = (0.5 * rng.standard_normal((H_kv, T, d)) + 0.3 * shared).astype(np.float32)
+    if cfg["dtype"] == "bf16":
+        q, kc = gen.f32_to_bf16_bits(qf), gen.f32_to_bf16_bits(kf)
+        kdt = K.KVSEL_BF16
+    else:
+        q, kc = qf, kf
+        kdt = K.KVSEL_F32
+    dev = "cuda"
+    kd = runner.to_device(kc[None], dev)
+    vd = torch.zeros_like(kd)
+    h = K.heads(H_q, H_kv, d, kdt)
+    p = K.Params(n_q, B)
+    prior = torch.tensor([T], dtype=torch.int64, device=dev)
+    b = K.batch([T], C, prior)
+    cache = K.cache(kd, vd, T)
+    ws = torch.empty(K.workspace_size(h, b, p), dtype=torch.uint8, device=dev)
+    nqp = min(n_q, C)
+    idx = torch.full((1, H_kv, B), -7, dtype=torch.int32, device=dev)
+    keep = torch.full((1, H_q, nqp), -7, dtype=torch.int32, device=dev)
+    S = torch.full((1, H_kv, T), float("nan"), dtype=torch.float32, device=dev)
+    K.kvsel_select(h, b, p, runner.to_device(q[None], dev), cache, idx, None, None, keep, S, ws)
+    torch.cuda.synchronize()
+    Q64, K64 = gen.to_f64(q), gen.to_f64(kc)
+    keep_h, S_h, idx_h = keep[0].cpu().numpy(), S[0].cpu().numpy(), idx[0].cpu().numpy()
+    for hh in range(H_q):
+        parity.check_keep(Q64[hh], n_q, keep_h[hh])
+    keep_list = [np.sort(keep_h[hh]) for hh in range(H_q)]
+    for g in range(H_kv):
+        S_or = quoka.key_scores(Q64[g * G:(g + 1) * G], keep_list[g * G:(g + 1) * G], K64[g:g + 1])[0]
+        parity.check_close(S_h[g], S_or, parity.S_TOL, f"S head {g}")
+        parity.check_idx(S_or, B, idx_h[g], S_h[g])
 
 
 def test_needles_are_recalled():
