@@ -277,6 +277,11 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x16{};
     float m = -INFINITY, l = 0.0f;
+    // kept beside m, updated only when it moves: the value the block max must
+    // pass to move it (m + 2^8 in log2 units) and -m * cl2 for the exponents
+    // (0 while no key is visible, so masked scores give 0)
+    float m_thr = -INFINITY, nmc = 0.0f;
+    const float step8 = 8.0f / cl2;
     float l2[2] = {0.0f, 0.0f};                 // row sum in two chains (l: their total at the end)
     const int krow = sigma(col);
     // K fragment of the S MFMA: key 32*kb2 + krow, elements 16*ks + 8*half .. +7
@@ -330,7 +335,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
             for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb2][r]);
             mt = half_max(mt);
             const float m_new = fmaxf(m, mt);
-            if (__ballot((m_new - m) * cl2 > 8.0f) != 0ull) {
+            if (__ballot(m_new > m_thr) != 0ull) {
                 const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m - m_new) * cl2);
                 l2[0] *= alpha;
                 l2[1] *= alpha;
@@ -339,8 +344,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
                 m = m_new;
+                m_thr = m + step8;
+                nmc = m == -INFINITY ? 0.0f : -m * cl2;   // no visible key yet: every p is 0
             }
-            const float mc = m == -INFINITY ? 0.0f : m * cl2;   // no visible key yet: every p is 0
             bf16x8 pf[2];
             KVSEL_SETPRIO(0);
 #pragma unroll
@@ -348,8 +354,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_mfma_kernel(const uint16_t
                 u32x4 w;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e], cl2, -mc));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e + 1], cl2, -mc));
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e], cl2, nmc));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e + 1], cl2, nmc));
                     w[e] = pack_bf16x2(p0, p1);
                     l2[e & 1] = add_pair(w[e], l2[e & 1]);
                 }
@@ -589,6 +595,8 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(const uint16_t* __restr
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x16{};
     float m = -INFINITY, l = 0.0f;
+    float m_thr = -INFINITY, nmc = 0.0f;    // as in attn_mfma_kernel
+    const float step8 = 8.0f / cl2;
     const int krow = sigma(col);
     const int lim = n_s + tok;
     f32x16 sacc[NKB];                       // S(t), from M(t) to X(t)
@@ -680,7 +688,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(const uint16_t* __restr
             for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb2][r]);
         mt = half_max(mt);
         const float m_new = fmaxf(m, mt);
-        if (__ballot((m_new - m) * cl2 > 8.0f) != 0ull) {
+        if (__ballot(m_new > m_thr) != 0ull) {
             const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m - m_new) * cl2);
             l *= alpha;
 #pragma unroll
@@ -688,8 +696,9 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(const uint16_t* __restr
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
             m = m_new;
+            m_thr = m + step8;
+            nmc = m == -INFINITY ? 0.0f : -m * cl2;
         }
-        const float mc = m == -INFINITY ? 0.0f : m * cl2;
 #pragma unroll
         for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
@@ -697,8 +706,8 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(const uint16_t* __restr
                 u32x4 w;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e], cl2, -mc));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e + 1], cl2, -mc));
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e], cl2, nmc));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][8 * k16 + 2 * e + 1], cl2, nmc));
                     l += p0 + p1;
                     w[e] = pack_bf16x2(p0, p1);
                 }
