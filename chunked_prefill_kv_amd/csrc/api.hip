@@ -316,7 +316,7 @@ kvsel_status check_ws(void* ws, size_t have, size_t need) {
 // Steps 1-3 into idx (shared by select and prefill_chunk).
 kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, const CacheView& cv, void* ws,
                         const Layout& L, int32_t* idx, int32_t* q_keep, float* scores, hipStream_t st,
-                        int32_t* rowidx = nullptr) {
+                        int32_t* rowidx = nullptr, const ChunkPack* cp = nullptr, bool* hosted = nullptr) {
     bool any = false;
     for (int i = 0; i < b->batch; ++i) any |= b->prior_len_host[i] > s.budget;
     const int64_t* T = b->prior_len_dev;
@@ -352,9 +352,10 @@ kvsel_status run_select(const SelShape& s, const kvsel_batch* b, const void* q, 
         KVSEL_TRY(traced(KVSEL_K_SCAN, st, [&] { return launch_scan(s, at<void>(ws, L.qsel), at<float>(ws, L.rq), cv, T, S, s.t_max, st, b->prior_len_host); }), "key scan");
     }
     float* comb = scores ? scores : S;
-    KVSEL_TRY(traced(KVSEL_K_TOPB, st, [&] { return launch_topb(s.batch * s.h_kv, s.h_kv, S, sc.nsplit, split_stride, comb, s.t_max, T,
-                                                                s.budget, s.t_max, any, at<uint32_t>(ws, L.topb), idx, st,
-                                                                rowidx ? &cv : nullptr, rowidx, b->prior_len_host); }), "key top-B");
+    KVSEL_TRY(traced(KVSEL_K_TOPB, st, [&] { return launch_topb_hosting(s.batch * s.h_kv, s.h_kv, S, sc.nsplit, split_stride, comb, s.t_max, T,
+                                                                        s.budget, s.t_max, any, at<uint32_t>(ws, L.topb), idx, st,
+                                                                        rowidx ? &cv : nullptr, rowidx, b->prior_len_host, cp, hosted); }),
+              "key top-B");
     return KVSEL_OK;
 }
 
@@ -382,14 +383,39 @@ kvsel_status run_prefill(const kvsel_heads* heads, const kvsel_batch* batch, con
     int32_t* idx_buf = idx ? idx : at<int32_t>(workspace, L.idx);
     const bool gather = prefill_uses_gather(s);
     int32_t* rowidx = gather ? at<int32_t>(workspace, L.rowidx) : nullptr;
-    if ((st = run_select(s, batch, q, cv, workspace, L, idx_buf, nullptr, nullptr, hs, rowidx))) return st;
+    const bool inplace = !gather && prefill_inplace(s, cache);
+    // bf16 key lists: their chunk slots and the cache append run in spare
+    // workgroups of the top-B threshold launch (most compute units are idle
+    // there), the pack launch then copies only the kept prior keys
+    ChunkPack cp{};
+    const bool host_chunk = !gather && !inplace && s.esz == 2;
+    if (host_chunk) {
+        cp.cv = cv;
+        cp.prior_len = batch->prior_len_dev;
+        cp.budget = s.budget;
+        cp.k_chunk = static_cast<const char*>(k_chunk);
+        cp.v_chunk = static_cast<const char*>(v_chunk);
+        cp.kall = at<char>(workspace, L.kall);
+        cp.vall = at<char>(workspace, L.vall);
+        cp.batch = s.batch;
+        cp.h_kv = s.h_kv;
+        cp.C = s.C;
+        cp.nk_pad = L.nk_pad;
+        cp.row_bytes = s.d * s.esz;
+        cp.wgs = chunk_pack_wgs(s.batch, s.h_kv, s.C);
+    }
+    bool hosted = false;
+    if ((st = run_select(s, batch, q, cv, workspace, L, idx_buf, nullptr, nullptr, hs, rowidx,
+                         host_chunk ? &cp : nullptr, &hosted)))
+        return st;
     PackSrc src{};
     src.cache = &cv;
     src.prior_len = batch->prior_len_dev;
     src.budget = s.budget;
     src.idx = idx_buf;
     src.idx_stride = s.budget;
-    src.append = true;
+    src.append = !hosted;
+    src.chunk_hosted = hosted;
     int32_t* nsel = at<int32_t>(workspace, L.nsel);
     const float scale = heads->scale > 0.0f ? heads->scale : 1.0f / std::sqrt(static_cast<float>(heads->d));
     if (gather) {
@@ -402,7 +428,7 @@ kvsel_status run_prefill(const kvsel_heads* heads, const kvsel_batch* batch, con
         KVSEL_TRY(traced(KVSEL_K_APPEND, hs, [&] { return launch_append(s, cv, batch->prior_len_dev, k_chunk, v_chunk, hs); }), "cache append");
         return KVSEL_OK;
     }
-    if (prefill_inplace(s, cache)) {
+    if (inplace) {
         // nothing selected: append the chunk, then the key list of every
         // (sequence, KV head) is its cache rows [0, T_b + C), read in place
         KVSEL_TRY(traced(KVSEL_K_APPEND, hs, [&] { return launch_append(s, cv, batch->prior_len_dev, k_chunk, v_chunk, hs); }), "cache append");

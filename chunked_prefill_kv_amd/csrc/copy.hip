@@ -33,6 +33,7 @@ struct PackArgs {
     char* vall;
     int32_t* nsel_out;
     bool append;             // also write the chunk's rows into the cache at [T_b, T_b + C)
+    bool chunk_hosted;       // tiles in [n_b, n_b + C) were written by the top-B launch
 };
 
 // Source rows of slot s (nullptr = zero row).
@@ -111,6 +112,7 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(PackArgs a) {
     int64_t T;
     const int nsel_b = seq_nsel(a, b, &T);
     if (a.nsel_out && g == 0 && tile == 0 && threadIdx.x == 0) a.nsel_out[b] = nsel_b;
+    if (a.chunk_hosted && tile * kTile >= nsel_b && tile * kTile < nsel_b + a.C) return;
     constexpr int PPT = kTile * PPR / 256;
     u32x4 kv[PPT], vv[PPT];
 #pragma unroll
@@ -226,6 +228,7 @@ hipError_t launch_pack(const SelShape& s, const PackSrc& src, const void* k_chun
     a.vall = static_cast<char*>(vall);
     a.nsel_out = nsel_out;
     a.append = src.append;
+    a.chunk_hosted = src.chunk_hosted && s.esz == 2;
     dim3 grid(s.batch * s.h_kv * a.tiles), block(256);
     if (s.esz == 2) {
         if (s.d == 128) hipLaunchKernelGGL(pack_bf16_kernel<128>, grid, block, 0, st, a);

@@ -121,11 +121,35 @@ int topb_segments(int64_t t_max, int64_t budget);
 size_t topb_scratch_bytes(int problems, int64_t t_max, int64_t budget);
 // Words at the start of the top-B scratch that must be zero on entry.
 size_t topb_zero_words(int problems);
+// The chunk's slots of the packed bf16 key lists ([bg][nk_pad][d] keys,
+// [bg][d][nk_pad] values) and the cache append, for a launch to run beside
+// its own work (chunk_pack.h); wgs = 0: nothing to run.
+struct ChunkPack {
+    CacheView cv;
+    const int64_t* prior_len;
+    int64_t budget;
+    const char* k_chunk;
+    const char* v_chunk;
+    char* kall;
+    char* vall;
+    int batch, h_kv, C, nk_pad, row_bytes;
+    int wgs;                          // workgroups added to the host launch
+};
+// Workgroups to add for `cp` (its item count, at most one per compute unit).
+int chunk_pack_wgs(int batch, int h_kv, int C);
 hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int nsplit, int64_t split_stride,
                        float* comb, int64_t s_stride, const int64_t* prior_len, int64_t budget, int64_t t_max,
                        bool any_select, uint32_t* scratch, int32_t* out, hipStream_t st,
                        const CacheView* cv = nullptr, int32_t* rowidx = nullptr,
                        const int64_t* prior_len_host = nullptr);
+// The same, with the chunk's part of the key lists run by extra workgroups of
+// the threshold launch when that launch happens (*hosted says whether it did;
+// if not, nothing of `cp` ran).
+hipError_t launch_topb_hosting(int problems, int heads_per_seq, const float* part, int nsplit, int64_t split_stride,
+                               float* comb, int64_t s_stride, const int64_t* prior_len, int64_t budget, int64_t t_max,
+                               bool any_select, uint32_t* scratch, int32_t* out, hipStream_t st,
+                               const CacheView* cv, int32_t* rowidx, const int64_t* prior_len_host,
+                               const ChunkPack* cp, bool* hosted);
 
 // Gather the kept query rows of every head into Q_sel[b][g][hh*nq_pad + r][d]
 // (raw rows) and rq = 1/|q|; rows r >= nqp repeat row 0 of that head.  With
@@ -181,6 +205,9 @@ struct PackSrc {
     int n_sel_max;
     // cache mode only: also append the chunk's rows to the cache at [T_b, T_b + C)
     bool append;
+    // the tiles from n_b to n_b + C (chunk rows only) were written by the
+    // top-B launch (ChunkPack): skip them
+    bool chunk_hosted;
 };
 hipError_t launch_pack(const SelShape& s, const PackSrc& src, const void* k_chunk, const void* v_chunk,
                        int nk_pad, void* kall, void* vall, int32_t* nsel_out, hipStream_t st);

@@ -16,7 +16,9 @@
 // For few short problems topb_thresh also does topb_hist's work (its
 // workgroup holds the problem's scores in registers).  With the prior lengths
 // on the host, the segment grids list only the segments that have keys.
-#include "launch.h"
+#include <algorithm>
+
+#include "chunk_pack.h"
 
 namespace kvsel {
 
@@ -51,6 +53,7 @@ struct TopbArgs {
     int32_t* out;             // [problem][budget]
     CacheView cv;             // with rowidx: the cache the positions index
     int32_t* rowidx;          // optional [problem][budget]: cache row number of each kept position
+    int problems;             // threshold workgroups; those past them run the ChunkPack items
 };
 
 }  // namespace
@@ -146,19 +149,24 @@ __device__ __forceinline__ uint32_t excl_scan_1024(uint32_t v, uint32_t* wsum) {
 constexpr int kFusedSteps = 4;                  // 8192-key steps held in registers
 constexpr int kFusedKeys = kFusedSteps * 8192;
 template <bool FUSED, int NST>
-__global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a) {
+__global__ __launch_bounds__(1024) void topb_thresh_kernel(TopbArgs a, ChunkPack cp) {
     static_assert(!FUSED || NST == kFusedSteps, "the fused form holds every step");
-    const int p = blockIdx.x;
-    const int64_t T64 = a.prior_len[p / a.heads_per_seq];
-    if (T64 <= a.budget) return;
-    const int T = static_cast<int>(T64);
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     __shared__ uint32_t hs[kBins];
     __shared__ uint32_t ck[kCap];
     __shared__ int cj[kCap];
     __shared__ uint32_t sgt[kTopbMaxSegments], seq_[kTopbMaxSegments];   // per-segment counts
     __shared__ uint32_t wsum[16];
     __shared__ uint32_t s_bin, s_need, s_cnt, s_digit, s_rem, s_full;
+    static_assert(sizeof(hs) >= 64 * 128 * 2, "the histogram holds a 64 x 128 bf16 staging tile");
+    if (static_cast<int>(blockIdx.x) >= a.problems) {      // spare workgroups: the chunk's key-list slots
+        chunk_pack_wg(cp, static_cast<int>(blockIdx.x) - a.problems, reinterpret_cast<uint16_t*>(hs));
+        return;
+    }
+    const int p = blockIdx.x;
+    const int64_t T64 = a.prior_len[p / a.heads_per_seq];
+    if (T64 <= a.budget) return;
+    const int T = static_cast<int>(T64);
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const float* c = a.comb + static_cast<int64_t>(p) * a.s_stride;
     // The scores pass over the keys in 8192-key steps (wave w takes
     // [base0 + 512 w, +512) in 8 loads of 64), held in a ring of NST steps of
@@ -487,10 +495,24 @@ size_t topb_scratch_bytes(int problems, int64_t t_max, int64_t budget) {
     return size_t(problems) * (kBins + 2 + 2 * size_t(nseg)) * 4;
 }
 
+int chunk_pack_wgs(int batch, int h_kv, int C) {
+    const int64_t items = int64_t(batch) * h_kv * ((C + 63) / 64 + 1);
+    return static_cast<int>(std::min<int64_t>(items, device_cus()));
+}
+
 hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int nsplit, int64_t split_stride,
                        float* comb, int64_t s_stride, const int64_t* prior_len, int64_t budget, int64_t t_max,
                        bool any_select, uint32_t* scratch, int32_t* out, hipStream_t st, const CacheView* cv,
                        int32_t* rowidx, const int64_t* prior_len_host) {
+    return launch_topb_hosting(problems, heads_per_seq, part, nsplit, split_stride, comb, s_stride, prior_len, budget,
+                               t_max, any_select, scratch, out, st, cv, rowidx, prior_len_host, nullptr, nullptr);
+}
+
+hipError_t launch_topb_hosting(int problems, int heads_per_seq, const float* part, int nsplit, int64_t split_stride,
+                               float* comb, int64_t s_stride, const int64_t* prior_len, int64_t budget, int64_t t_max,
+                               bool any_select, uint32_t* scratch, int32_t* out, hipStream_t st, const CacheView* cv,
+                               int32_t* rowidx, const int64_t* prior_len_host, const ChunkPack* cp, bool* hosted) {
+    if (hosted) *hosted = false;
     TopbArgs a;
     a.cv = cv ? *cv : CacheView{};
     a.rowidx = cv ? rowidx : nullptr;
@@ -524,9 +546,17 @@ hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int n
     if (build_tile_map(mw, prior_len_host, batch, heads_per_seq, full,
                        [&](int64_t T) -> int64_t { return ((T > budget ? T : budget) + kSeg - 1) / kSeg; }))
         grid_w = dim3(static_cast<unsigned>(mw.first[batch]));
+    a.problems = problems;
     if (any_select && grid_h.x > 0) {
+        // the threshold launch hosts the chunk's key-list slots when asked
+        // (at most one workgroup per compute unit beside the thresholds')
+        ChunkPack c = cp ? *cp : ChunkPack{};
+        if (!cp) c.wgs = 0;
+        else if (problems < device_cus()) c.wgs = std::min(c.wgs, device_cus() - problems);
+        const dim3 grid_t(static_cast<unsigned>(problems + c.wgs));
+        if (hosted) *hosted = c.wgs > 0;
         if (fused) {
-            hipLaunchKernelGGL((topb_thresh_kernel<true, kFusedSteps>), dim3(problems), dim3(1024), 0, st, a);
+            hipLaunchKernelGGL((topb_thresh_kernel<true, kFusedSteps>), grid_t, dim3(1024), 0, st, a, c);
         } else {
             if (nsplit > 1) hipLaunchKernelGGL(topb_hist_kernel<true>, grid_h, dim3(256), 0, st, a, mh);
             else hipLaunchKernelGGL(topb_hist_kernel<false>, grid_h, dim3(256), 0, st, a, mh);
@@ -535,9 +565,9 @@ hipError_t launch_topb(int problems, int heads_per_seq, const float* part, int n
             // step, and more workgroups share each CU (on the 512-problem
             // decode batch: 101 us per step against 113 with four)
             if (problems < device_cus())
-                hipLaunchKernelGGL((topb_thresh_kernel<false, 4>), dim3(problems), dim3(1024), 0, st, a);
+                hipLaunchKernelGGL((topb_thresh_kernel<false, 4>), grid_t, dim3(1024), 0, st, a, c);
             else
-                hipLaunchKernelGGL((topb_thresh_kernel<false, 1>), dim3(problems), dim3(1024), 0, st, a);
+                hipLaunchKernelGGL((topb_thresh_kernel<false, 1>), grid_t, dim3(1024), 0, st, a, c);
         }
     }
     if (grid_w.x > 0) hipLaunchKernelGGL(topb_write_kernel, grid_w, dim3(256), 0, st, a, mw);
