@@ -24,15 +24,16 @@ namespace kvsel {
 __device__ inline void chunk_pack_wg(const ChunkPack& c, int w, uint16_t* lds) {
     const int D = c.row_bytes / 2, PPR = D / 8;        // bf16 elements and 16-byte pieces per row
     const int jt = (c.C + 63) / 64 + 1;                // tiles a chunk can touch
-    const int items = c.batch * c.h_kv * jt;
+    const int64_t items = static_cast<int64_t>(c.batch) * c.h_kv * jt;
     const int nt = blockDim.x, tid = threadIdx.x;
-    for (int i = w; i < items; i += c.wgs) {           // uniform per workgroup
-        const int bg = i / jt, j = i % jt;
+    for (int64_t i = w; i < items; i += c.wgs) {       // uniform per workgroup
+        const int bg = static_cast<int>(i / jt), j = static_cast<int>(i % jt);
         const int b = bg / c.h_kv, g = bg % c.h_kv;
         const int64_t T = c.prior_len[b];
         const int n = static_cast<int>(T < c.budget ? T : c.budget);
-        const int s0 = (n / 64 + j) * 64;
-        if (s0 >= n + c.C || s0 >= c.nk_pad) continue;
+        const int64_t s0l = (static_cast<int64_t>(n) / 64 + j) * 64;
+        if (s0l >= static_cast<int64_t>(n) + c.C || s0l >= c.nk_pad) continue;
+        const int s0 = static_cast<int>(s0l);
         const bool whole = s0 >= n;                    // no kept prior key in this tile
         for (int p = tid; p < 64 * PPR; p += nt) {
             const int r = p / PPR, cc = p % PPR;
