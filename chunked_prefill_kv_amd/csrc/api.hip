@@ -405,7 +405,10 @@ kvsel_status run_prefill(const kvsel_heads* heads, const kvsel_batch* batch, con
         cp.wgs = chunk_pack_wgs(s.batch, s.h_kv, s.C);
     }
     bool hosted = false;
-    if ((st = run_select(s, batch, q, cv, workspace, L, idx_buf, nullptr, nullptr, hs, rowidx,
+    // nothing to select and no index output asked for: the in-place attention
+    // reads no index, so the identity index write is skipped
+    if (!(inplace && !idx) &&
+        (st = run_select(s, batch, q, cv, workspace, L, idx_buf, nullptr, nullptr, hs, rowidx,
                          host_chunk ? &cp : nullptr, &hosted)))
         return st;
     PackSrc src{};
