@@ -296,9 +296,11 @@ typedef enum {
     KVSEL_K_QTOPK = 1,    /* step 1: the kept queries (exact top-k) */
     KVSEL_K_QPACK = 2,    /* step 1: kept query rows packed per KV head */
     KVSEL_K_SCAN = 3,     /* step 2: cosine key scores over the prior cache */
-    KVSEL_K_TOPB = 4,     /* step 3: per-KV-head top-B */
+    KVSEL_K_TOPB = 4,     /* step 3: per-KV-head top-B (in kvsel_prefill_chunk's bf16 packed path its
+                             threshold launch also writes the chunk's list slots and appends the chunk) */
     KVSEL_K_GATHER = 5,   /* step 4 (kvsel_select): k_sel/v_sel rows */
-    KVSEL_K_PACK = 6,     /* step 4: compacted keys + chunk keys for attention, and the cache append */
+    KVSEL_K_PACK = 6,     /* step 4: compacted keys (+ chunk keys and the cache append, unless the
+                             top-B launch wrote them) for attention */
     KVSEL_K_ATTN = 7,     /* step 5: attention */
     KVSEL_K_APPEND = 8,   /* cache append on its own (gathering attention path; otherwise inside the pack kernel) */
     KVSEL_K_QPOOL = 9,    /* step 1 with KVSEL_POOL_GROUP: the group's unit queries averaged per token */
